@@ -1,0 +1,24 @@
+"""Seeded synthetic inputs for the masked-attention forward.
+
+Shapes, sequence lengths, per-token id layouts, page tables and random
+values only: nothing here computes a mask, a score or a softmax. Both the
+CPU oracle tests and the HIP path tests draw their inputs from this package.
+"""
+
+from .workloads import (  # noqa: F401
+    THINK_ROLE,
+    KINDS,
+    Layout,
+    causal_single,
+    full_single,
+    packed_documents,
+    shared_prefix,
+    strip_thinking,
+    paged_decode,
+    config,
+    CONFIG_NAMES,
+    random_layout,
+    make_dense_qkv,
+    make_paged_kv,
+    derive_seed,
+)

@@ -1,0 +1,165 @@
+"""Pins of oracle.masks against the pages and independent constructions (CPU)."""
+
+import numpy as np
+import pytest
+
+import _golden
+import synth
+from oracle import masks
+
+
+def test_causal_mask_matches_printed_4x4():
+    # Ch. 9, Worked Example 9.1.1: the causal mask applied to 1..16.
+    g = _golden.load("causal_mask_4x4.txt")
+    vis = masks.visible("causal", 4, 4)
+    assert np.array_equal(np.where(vis, g["input"], 0.0), g["causal"])
+    # Worked Example 9.1.2: the strict comparison is the printed bug; the
+    # oracle's mask must not reproduce it.
+    assert not np.array_equal(np.where(vis, g["input"], 0.0), g["strict"])
+    strict = np.arange(4)[None, :] < np.arange(4)[:, None]
+    assert np.array_equal(np.where(strict, g["input"], 0.0), g["strict"])
+
+
+def test_causal_equals_lower_triangle_library():
+    for L in (1, 2, 7, 33):
+        assert np.array_equal(masks.visible("causal", L, L), np.tril(np.ones((L, L), bool)))
+
+
+def test_decode_query_sees_whole_context():
+    # One query at the end of its context sees every key (the decode reading).
+    for Lk in (1, 5, 17):
+        vis = masks.visible("causal", 1, Lk)
+        assert vis.shape == (1, Lk) and vis.all()
+    # Several trailing queries: the bottom-right part of the full triangle.
+    Lq, Lk = 3, 9
+    assert np.array_equal(masks.visible("causal", Lq, Lk),
+                          np.tril(np.ones((Lk, Lk), bool))[Lk - Lq:])
+
+
+def _shared_prefix_by_sets(seg):
+    """Visible sets built from the segment layout, not from the predicate:
+    prefix tokens see the prefix up to themselves; a token of suffix i sees the
+    whole prefix part that precedes it plus its own suffix up to itself."""
+    T = len(seg)
+    vis = np.zeros((T, T), bool)
+    for qpos in range(T):
+        if seg[qpos] == 0:
+            allowed = [j for j in range(qpos + 1) if seg[j] == 0]
+        else:
+            allowed = [j for j in range(qpos + 1) if seg[j] == 0] + \
+                      [j for j in range(qpos + 1) if seg[j] == seg[qpos]]
+        vis[qpos, sorted(set(allowed))] = True
+    return vis
+
+
+def test_shared_prefix_matches_set_construction():
+    lay = synth.shared_prefix(prefix=5, n_suffix=3, suffix=4, H=1, D=8)
+    seg = lay.seg_k
+    vis = masks.visible("shared_prefix", len(seg), len(seg), seg_q=seg, seg_k=seg)
+    assert np.array_equal(vis, _shared_prefix_by_sets(seg))
+    # Suffix 2 never sees suffix 1.
+    s1 = np.nonzero(seg == 1)[0]
+    s2 = np.nonzero(seg == 2)[0]
+    assert not vis[np.ix_(s2, s1)].any()
+
+
+def test_shared_prefix_reductions():
+    rng = np.random.default_rng(3)
+    for L in (1, 6, 20):
+        zero = np.zeros(L, np.int32)
+        assert np.array_equal(masks.visible("shared_prefix", L, L, seg_q=zero, seg_k=zero),
+                              masks.visible("causal", L, L))
+        ids = rng.integers(0, 4, size=L).astype(np.int32)
+        sp = masks.visible("shared_prefix", L, L, seg_q=ids, seg_k=ids)
+        assert not (sp & ~masks.visible("causal", L, L)).any()
+        assert np.array_equal(np.diag(sp), np.ones(L, bool))  # diagonal always kept
+
+
+def test_shared_prefix_position_reading_equivalent():
+    # The causal test on the packed index equals the one on position_ids that
+    # restart at len(P) for every suffix (the page's position convention).
+    P, n, S = 6, 3, 5
+    lay = synth.shared_prefix(prefix=P, n_suffix=n, suffix=S, H=1, D=8)
+    seg = lay.seg_k
+    pos = np.concatenate([np.arange(P)] + [P + np.arange(S) for _ in range(n)])
+    T = len(seg)
+    by_pos = np.zeros((T, T), bool)
+    for i in range(T):
+        for j in range(T):
+            by_pos[i, j] = (pos[i] >= pos[j]) and (seg[j] == 0 or seg[j] == seg[i])
+    assert np.array_equal(masks.visible("shared_prefix", T, T, seg_q=seg, seg_k=seg), by_pos)
+
+
+def _strip_thinking_by_spans(role, turn, think):
+    """A query at position p of turn t sees positions <= p minus the think
+    spans of every earlier turn (built from span lists)."""
+    T = len(role)
+    spans = {}
+    for j in range(T):
+        if role[j] == think:
+            spans.setdefault(int(turn[j]), []).append(j)
+    vis = np.zeros((T, T), bool)
+    for p in range(T):
+        hidden = set()
+        for t, js in spans.items():
+            if t < turn[p]:
+                hidden.update(js)
+        for j in range(p + 1):
+            if j not in hidden:
+                vis[p, j] = True
+    return vis
+
+
+def test_strip_thinking_matches_span_construction():
+    lay = synth.strip_thinking(n_turns=3, user=2, think=3, answer=2, H=1, D=8)
+    role, turn = lay.role_k, lay.turn_k
+    T = len(role)
+    vis = masks.visible("strip_thinking", T, T, role_k=role, turn_q=turn, turn_k=turn,
+                        think_role=synth.THINK_ROLE)
+    assert np.array_equal(vis, _strip_thinking_by_spans(role, turn, synth.THINK_ROLE))
+    # The query's own-turn thinking stays visible: answer of turn 1 sees think of turn 1.
+    a1 = np.nonzero((role == 2) & (turn == 1))[0]
+    k1 = np.nonzero((role == synth.THINK_ROLE) & (turn == 1))[0]
+    assert vis[np.ix_(a1, k1)].all()
+    k0 = np.nonzero((role == synth.THINK_ROLE) & (turn == 0))[0]
+    assert not vis[np.ix_(a1, k0)].any()
+
+
+def test_strip_thinking_random_layouts_match_spans():
+    rng = np.random.default_rng(11)
+    for _ in range(5):
+        lay = synth.random_layout(rng, "strip_thinking", n_seqs=1, max_len=30)
+        T = lay.seqlens_k[0]
+        vis = masks.visible("strip_thinking", T, T, role_k=lay.role_k, turn_q=lay.turn_q,
+                            turn_k=lay.turn_k)
+        assert np.array_equal(vis, _strip_thinking_by_spans(lay.role_k, lay.turn_k, 1))
+
+
+def test_strip_thinking_without_think_is_causal():
+    L = 12
+    role = np.array([0, 2] * 6, np.int32)
+    turn = np.repeat(np.arange(6), 2).astype(np.int32)
+    assert np.array_equal(masks.visible("strip_thinking", L, L, role_k=role, turn_q=turn,
+                                        turn_k=turn),
+                          masks.visible("causal", L, L))
+
+
+def test_packed_documents_block_diagonal():
+    # Each document is its own sequence: concatenating the per-sequence masks
+    # on the packed axis gives the block-diagonal causal mask of the batch.
+    lens = [3, 1, 4]
+    T = sum(lens)
+    big = np.zeros((T, T), bool)
+    o = 0
+    for L in lens:
+        big[o:o + L, o:o + L] = masks.visible("causal", L, L)
+        o += L
+    doc = np.repeat(np.arange(len(lens)), lens)
+    expect = (np.arange(T)[None, :] <= np.arange(T)[:, None]) & (doc[:, None] == doc[None, :])
+    assert np.array_equal(big, expect)
+
+
+def test_full_mask():
+    assert masks.visible("full", 3, 5).all()
+    with pytest.raises(ValueError):
+        masks.visible("bogus", 2, 2)

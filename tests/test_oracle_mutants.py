@@ -1,0 +1,167 @@
+"""Planted mistakes in the oracle must fail at least one pin (CPU).
+
+Each mutant replaces one oracle function with a plausibly wrong version (a
+strict comparison, a dropped scale, a wrong index, a missing rescale ...)
+and runs pins from the other test modules, which must raise.
+"""
+
+import numpy as np
+import pytest
+
+import test_oracle_attention as ta
+import test_oracle_masks as tm
+import test_oracle_paged as tp
+import test_oracle_tiles as tt
+from oracle import attention, masks, paged, tiles
+
+
+def _fails(*pins):
+    failed = 0
+    for pin in pins:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            failed += 1
+    return failed
+
+
+def test_mutant_strict_causal(monkeypatch):
+    orig = masks.visible
+
+    def strict(kind, Lq, Lk, **kw):
+        vis = orig(kind, Lq, Lk, **kw)
+        if kind != "full":
+            qi = masks.query_positions(Lq, Lk)[:, None]
+            vis = vis & (np.arange(Lk)[None, :] != qi)
+        return vis
+
+    monkeypatch.setattr(masks, "visible", strict)
+    assert _fails(tm.test_causal_mask_matches_printed_4x4, tm.test_causal_equals_lower_triangle_library,
+                  tt.test_tile_classes_match_printed_diagram) >= 1
+
+
+def test_mutant_shared_prefix_wrong_side(monkeypatch):
+    orig = masks.visible
+
+    def wrong(kind, Lq, Lk, **kw):
+        if kind == "shared_prefix":  # tests the query's segment for 0 instead of the key's
+            sq = np.asarray(kw["seg_q"])[:, None]
+            sk = np.asarray(kw["seg_k"])[None, :]
+            return orig("causal", Lq, Lk) & ((sq == 0) | (sk == sq))
+        return orig(kind, Lq, Lk, **kw)
+
+    monkeypatch.setattr(masks, "visible", wrong)
+    assert _fails(tm.test_shared_prefix_matches_set_construction,
+                  ta.test_shared_prefix_suffix_equals_prefix_plus_suffix_alone) >= 1
+
+
+def test_mutant_strip_thinking_le(monkeypatch):
+    orig = masks.visible
+
+    def wrong(kind, Lq, Lk, **kw):
+        if kind == "strip_thinking":  # hides the query's own-turn thinking too
+            tq = np.asarray(kw["turn_q"])[:, None]
+            tk = np.asarray(kw["turn_k"])[None, :]
+            rk = np.asarray(kw["role_k"])[None, :]
+            return orig("causal", Lq, Lk) & ~((rk == 1) & (tk <= tq))
+        return orig(kind, Lq, Lk, **kw)
+
+    monkeypatch.setattr(masks, "visible", wrong)
+    assert _fails(tm.test_strip_thinking_matches_span_construction,
+                  ta.test_strip_thinking_last_turn_equals_deleted_think_spans) >= 1
+
+
+def test_mutant_dropped_scale(monkeypatch):
+    orig = attention.three_pass
+    monkeypatch.setattr(attention, "three_pass",
+                        lambda q, k, v, vis, scale, **kw: orig(q, k, v, vis, 1.0, **kw))
+    assert _fails(ta.test_noncausal_vs_causal_printed_difference,
+                  ta.test_noncausal_matches_library_softmax) >= 1
+
+
+def test_mutant_transposed_value_weighting(monkeypatch):
+    orig = attention.three_pass
+
+    def wrong(q, k, v, vis, scale, **kw):  # weights the keys instead of the values
+        return orig(q, k, k[:, :np.asarray(v).shape[1]] if hasattr(k, "shape") else k, vis, scale)
+
+    monkeypatch.setattr(attention, "three_pass", wrong)
+    assert _fails(ta.test_noncausal_matches_library_softmax, ta.test_single_visible_key_closed_form) >= 1
+
+
+def test_mutant_online_without_acc_rescale(monkeypatch):
+    def wrong(q, k, v, vis, scale, BM, BN, skip_empty=True):
+        q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+        Lq, Lk = vis.shape
+        O = np.zeros((Lq, v.shape[1]))
+        lse = np.full(Lq, -np.inf)
+        for r0 in range(0, Lq, BM):
+            r1 = min(Lq, r0 + BM)
+            m = np.full(r1 - r0, -np.inf)
+            l = np.zeros(r1 - r0)
+            acc = np.zeros((r1 - r0, v.shape[1]))
+            for c0 in range(0, Lk, BN):
+                c1 = min(Lk, c0 + BN)
+                s = np.where(vis[r0:r1, c0:c1], q[r0:r1] @ k[c0:c1].T * scale, -np.inf)
+                m_new = np.maximum(m, s.max(axis=1))
+                mu = np.where(np.isneginf(m_new), 0, m_new)
+                alpha = np.exp(m - mu)
+                p = np.exp(s - mu[:, None])
+                l = alpha * l + p.sum(1)
+                acc = acc + p @ v[c0:c1]  # the rescale of acc is missing
+                m = m_new
+            O[r0:r1] = acc / np.where(l > 0, l, 1)[:, None]
+            lse[r0:r1] = m + np.log(np.where(l > 0, l, 1))
+        return O, lse
+
+    monkeypatch.setattr(attention, "online_tiled", wrong)
+    with pytest.raises(AssertionError):
+        ta.test_online_tiled_independent_of_block_size("causal")
+
+
+def test_mutant_edge_tiles_full(monkeypatch):
+    def wrong(vis, BM, BN, n_qt=None, n_kt=None):  # forgets that padding is not visible
+        Lq, Lk = vis.shape
+        n_qt = tiles.cdiv(Lq, BM) if n_qt is None else n_qt
+        n_kt = tiles.cdiv(Lk, BN) if n_kt is None else n_kt
+        cls = np.zeros((n_qt, n_kt), np.uint8)
+        for a in range(n_qt):
+            for b in range(n_kt):
+                blk = vis[a * BM:(a + 1) * BM, b * BN:(b + 1) * BN]
+                if blk.size == 0 or not blk.any():
+                    cls[a, b] = tiles.EMPTY
+                elif blk.all():
+                    cls[a, b] = tiles.FULL
+                else:
+                    cls[a, b] = tiles.PARTIAL
+        return cls
+
+    monkeypatch.setattr(tiles, "classify", wrong)
+    assert _fails(tt.test_causal_classes_match_closed_form, tt.test_edge_tiles_never_full) >= 1
+
+
+def test_mutant_gather_page_slot_swapped(monkeypatch):
+    def wrong(pool, bt, ctx, page_size, tile=None):
+        pool = np.asarray(pool)
+        flat = pool.reshape((-1,) + pool.shape[2:])
+        j = np.arange(ctx)
+        bt = np.asarray(bt, np.int64)
+        rows = bt[j % len(bt)] * page_size + j // page_size  # page and slot swapped
+        rows = np.clip(rows, 0, flat.shape[0] - 1)
+        return flat[rows]
+
+    monkeypatch.setattr(paged, "paged_gather", wrong)
+    assert _fails(tp.test_gather_byte_equal_for_every_tile_size) >= 1
+
+
+def test_mutant_gather_reads_past_context(monkeypatch):
+    orig = paged.paged_gather
+
+    def wrong(pool, bt, ctx, page_size, tile=None):  # gathers whole pages
+        n = -(-ctx // page_size)
+        return orig(pool, bt, n * page_size, page_size, tile)
+
+    monkeypatch.setattr(paged, "paged_gather", wrong)
+    import oracle.forward as of
+    monkeypatch.setattr(of, "paged_gather", wrong)
+    assert _fails(tp.test_ragged_rows_through_pages, tp.test_gather_byte_equal_for_every_tile_size) >= 1
