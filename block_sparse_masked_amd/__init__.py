@@ -1,0 +1,21 @@
+"""Block-sparse masked attention forward for AMD MI355X (gfx950).
+
+The computation lives in the HIP library ``lib/libbmattn.so`` (C ABI in
+include/bmattn.h); ``bmattn`` is its ctypes binding.  Build it with
+``python -m block_sparse_masked_amd.build``.
+"""
+
+from . import bmattn  # noqa: F401
+
+bmattn.lib()  # fail loudly at import when the HIP library is not built
+from .bmattn import (  # noqa: F401
+    BlockMask,
+    BmattnError,
+    MaskDesc,
+    build_block_mask,
+    debug_dense_mask,
+    forward,
+    forward_workspace_size,
+    paged_gather,
+    validate,
+)

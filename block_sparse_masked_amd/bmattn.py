@@ -1,0 +1,319 @@
+"""Python binding of libbmattn (ctypes; argument marshalling only).
+
+Every step of the computation runs in the HIP library.  PyTorch provides
+device memory and the current stream; this module only fills the C structs
+declared in include/bmattn.h, allocates outputs with torch, and raises
+``BmattnError`` on a non-zero status.  If the built library is missing the
+import fails loudly: there is no other implementation behind these names.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libbmattn.so")
+
+MASK_FULL, MASK_CAUSAL, MASK_SHARED_PREFIX, MASK_STRIP_THINKING = 0, 1, 2, 3
+KIND_CODES = {"full": MASK_FULL, "causal": MASK_CAUSAL, "shared_prefix": MASK_SHARED_PREFIX,
+              "strip_thinking": MASK_STRIP_THINKING}
+F32, BF16 = 0, 1
+TILE_EMPTY, TILE_PARTIAL, TILE_FULL = 0, 1, 2
+STATUS = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "EALIGN", 4: "EHIP", 5: "EWORKSPACE"}
+
+EXPORTS = ("bmattn_block_mask_shape", "bmattn_build_block_mask", "bmattn_forward_workspace_size",
+           "bmattn_forward", "bmattn_paged_gather", "bmattn_debug_dense_mask", "bmattn_validate",
+           "bmattn_status_string", "bmattn_last_error", "bmattn_abi_version")
+
+_p = ctypes.c_void_p
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+class MaskDescC(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("n_seqs", ctypes.c_int32),
+                ("max_seqlen_q", ctypes.c_int32), ("max_seqlen_k", ctypes.c_int32),
+                ("total_q", ctypes.c_int64), ("total_k", ctypes.c_int64),
+                ("think_role", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("cu_seqlens_q", _p), ("cu_seqlens_k", _p), ("seg_q", _p), ("seg_k", _p),
+                ("role_k", _p), ("turn_q", _p), ("turn_k", _p)]
+
+
+class BlockMaskC(ctypes.Structure):
+    _fields_ = [("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
+                ("n_seqs", ctypes.c_int32), ("n_qt", ctypes.c_int32), ("n_kt", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32),
+                ("tile_class", _p), ("full_cnt", _p), ("part_cnt", _p), ("full_idx", _p),
+                ("part_idx", _p), ("row_order", _p)]
+
+
+class FwdArgsC(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("q", _p), ("q_stride_tok", ctypes.c_int64), ("q_stride_head", ctypes.c_int64),
+                ("k", _p), ("k_stride_tok", ctypes.c_int64), ("k_stride_head", ctypes.c_int64),
+                ("v", _p), ("v_stride_tok", ctypes.c_int64), ("v_stride_head", ctypes.c_int64),
+                ("o", _p), ("o_stride_tok", ctypes.c_int64), ("o_stride_head", ctypes.c_int64),
+                ("lse", _p), ("lse_stride_head", ctypes.c_int64),
+                ("block_table", _p), ("block_table_stride", ctypes.c_int64),
+                ("num_pages", ctypes.c_int64), ("scale", ctypes.c_float),
+                ("reserved0", ctypes.c_int32), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class BmattnError(RuntimeError):
+    def __init__(self, status: int, fn: str, msg: str):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded library (loaded once; raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libbmattn is not built ({LIB_PATH} missing): run "
+                              "python -m block_sparse_masked_amd.build")
+        L = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_GLOBAL)
+        L.bmattn_status_string.restype = ctypes.c_char_p
+        L.bmattn_last_error.restype = ctypes.c_char_p
+        L.bmattn_abi_version.restype = ctypes.c_int
+        L.bmattn_block_mask_shape.argtypes = [ctypes.POINTER(MaskDescC), ctypes.c_int32,
+                                              ctypes.c_int32, _i32p, _i32p,
+                                              ctypes.POINTER(ctypes.c_int64),
+                                              ctypes.POINTER(ctypes.c_int64)]
+        L.bmattn_build_block_mask.argtypes = [ctypes.POINTER(MaskDescC), ctypes.POINTER(BlockMaskC), _p]
+        L.bmattn_forward_workspace_size.argtypes = [ctypes.POINTER(FwdArgsC), ctypes.POINTER(MaskDescC),
+                                                    ctypes.POINTER(BlockMaskC),
+                                                    ctypes.POINTER(ctypes.c_size_t)]
+        L.bmattn_forward.argtypes = [ctypes.POINTER(FwdArgsC), ctypes.POINTER(MaskDescC),
+                                     ctypes.POINTER(BlockMaskC), _p]
+        L.bmattn_paged_gather.argtypes = [_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int64, _p, ctypes.c_int64,
+                                          ctypes.POINTER(MaskDescC), _p, _p]
+        L.bmattn_debug_dense_mask.argtypes = [ctypes.POINTER(MaskDescC), ctypes.POINTER(BlockMaskC),
+                                              ctypes.c_int32, _p, ctypes.c_int64, _p]
+        L.bmattn_validate.argtypes = [ctypes.POINTER(MaskDescC), _p, ctypes.c_int64, ctypes.c_int32,
+                                      ctypes.c_int64, _p, _p]
+        for name in EXPORTS:
+            getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int, fn: str):
+    if status != 0:
+        raise BmattnError(status, fn, lib().bmattn_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _i32(t: Optional[torch.Tensor], device) -> Optional[torch.Tensor]:
+    if t is None:
+        return None
+    t = torch.as_tensor(t)
+    return t.to(device=device, dtype=torch.int32).contiguous()
+
+
+@dataclass
+class MaskDesc:
+    """A mask description (owns its device id arrays)."""
+
+    kind: int
+    n_seqs: int
+    max_seqlen_q: int
+    max_seqlen_k: int
+    total_q: int
+    total_k: int
+    cu_seqlens_q: torch.Tensor
+    cu_seqlens_k: torch.Tensor
+    seg_q: Optional[torch.Tensor] = None
+    seg_k: Optional[torch.Tensor] = None
+    role_k: Optional[torch.Tensor] = None
+    turn_q: Optional[torch.Tensor] = None
+    turn_k: Optional[torch.Tensor] = None
+    think_role: int = 1
+
+    @staticmethod
+    def create(kind, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, *,
+               device="cuda", seg_q=None, seg_k=None, role_k=None, turn_q=None, turn_k=None,
+               think_role: int = 1) -> "MaskDesc":
+        kind = KIND_CODES[kind] if isinstance(kind, str) else int(kind)
+        cq = _i32(cu_seqlens_q, device)
+        ck = _i32(cu_seqlens_k, device)
+        n = int(cq.numel()) - 1
+        tq = int(cq[-1].item()) if n >= 0 else 0
+        tk = int(ck[-1].item()) if n >= 0 else 0
+        return MaskDesc(kind, n, int(max_seqlen_q), int(max_seqlen_k), tq, tk, cq, ck,
+                        _i32(seg_q, device), _i32(seg_k, device), _i32(role_k, device),
+                        _i32(turn_q, device), _i32(turn_k, device), int(think_role))
+
+    def c(self) -> MaskDescC:
+        return MaskDescC(self.kind, self.n_seqs, self.max_seqlen_q, self.max_seqlen_k,
+                         self.total_q, self.total_k, self.think_role, 0,
+                         _ptr(self.cu_seqlens_q), _ptr(self.cu_seqlens_k), _ptr(self.seg_q),
+                         _ptr(self.seg_k), _ptr(self.role_k), _ptr(self.turn_q), _ptr(self.turn_k))
+
+
+@dataclass
+class BlockMask:
+    """Device arrays of a block mask (see bmattn_block_mask in include/bmattn.h)."""
+
+    block_m: int
+    block_n: int
+    n_seqs: int
+    n_qt: int
+    n_kt: int
+    tile_class: torch.Tensor
+    full_cnt: torch.Tensor
+    part_cnt: torch.Tensor
+    full_idx: torch.Tensor
+    part_idx: torch.Tensor
+    row_order: torch.Tensor
+
+    def c(self) -> BlockMaskC:
+        return BlockMaskC(self.block_m, self.block_n, self.n_seqs, self.n_qt, self.n_kt, 0,
+                          _ptr(self.tile_class), _ptr(self.full_cnt), _ptr(self.part_cnt),
+                          _ptr(self.full_idx), _ptr(self.part_idx), _ptr(self.row_order))
+
+
+def block_mask_shape(desc: MaskDesc, block_m: int, block_n: int):
+    n_qt, n_kt = ctypes.c_int32(), ctypes.c_int32()
+    rows, tiles = ctypes.c_int64(), ctypes.c_int64()
+    d = desc.c()
+    _check(lib().bmattn_block_mask_shape(ctypes.byref(d), block_m, block_n, ctypes.byref(n_qt),
+                                         ctypes.byref(n_kt), ctypes.byref(rows),
+                                         ctypes.byref(tiles)), "bmattn_block_mask_shape")
+    return n_qt.value, n_kt.value, rows.value, tiles.value
+
+
+def alloc_block_mask(desc: MaskDesc, block_m: int, block_n: int, device="cuda") -> BlockMask:
+    n_qt, n_kt, rows, tiles = block_mask_shape(desc, block_m, block_n)
+    i32 = dict(dtype=torch.int32, device=device)
+    return BlockMask(block_m, block_n, desc.n_seqs, n_qt, n_kt,
+                     torch.empty(tiles, dtype=torch.uint8, device=device),
+                     torch.empty(rows, **i32), torch.empty(rows, **i32),
+                     torch.empty(tiles, **i32), torch.empty(tiles, **i32), torch.empty(rows, **i32))
+
+
+def build_block_mask(desc: MaskDesc, block_m: int, block_n: int, out: Optional[BlockMask] = None,
+                     stream=None) -> BlockMask:
+    """bmattn_build_block_mask: tile classes, kv-tile lists and row schedule."""
+    bm = alloc_block_mask(desc, block_m, block_n, desc.cu_seqlens_q.device) if out is None else out
+    d, t = desc.c(), bm.c()
+    _check(lib().bmattn_build_block_mask(ctypes.byref(d), ctypes.byref(t), _stream(stream)),
+           "bmattn_build_block_mask")
+    return bm
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return BF16
+    if dt == torch.float32:
+        return F32
+    raise BmattnError(2, "forward", f"dtype {dt} is not supported")
+
+
+def _fwd_args(q, k, v, o, lse, *, block_table=None, page_size=0, scale=0.0, workspace=None):
+    H, D = q.shape[-2], q.shape[-1]
+    if block_table is not None:
+        # pools [num_pages, page_size, H, D]: token stride is per pool row
+        num_pages = k.shape[0]
+        page_size = k.shape[1]
+        kst, ksh = k.stride(1), k.stride(2)
+        vst, vsh = v.stride(1), v.stride(2)
+        bt_stride = block_table.stride(0)
+    else:
+        num_pages = 0
+        kst, ksh = k.stride(0), k.stride(1)
+        vst, vsh = v.stride(0), v.stride(1)
+        bt_stride = 0
+    return FwdArgsC(_dtype_code(q.dtype), H, D, int(page_size), _ptr(q), q.stride(0), q.stride(1),
+                    _ptr(k), kst, ksh, _ptr(v), vst, vsh, _ptr(o), o.stride(0), o.stride(1),
+                    _ptr(lse), 0 if lse is None else lse.stride(0), _ptr(block_table), bt_stride,
+                    num_pages, float(scale), 0, _ptr(workspace),
+                    0 if workspace is None else workspace.numel() * workspace.element_size())
+
+
+def forward_workspace_size(q, k, v, desc: MaskDesc, tiles: BlockMask, *, block_table=None) -> int:
+    o = q  # only shapes and strides are read
+    a = _fwd_args(q, k, v, o, None, block_table=block_table)
+    n = ctypes.c_size_t()
+    d, t = desc.c(), tiles.c()
+    _check(lib().bmattn_forward_workspace_size(ctypes.byref(a), ctypes.byref(d), ctypes.byref(t),
+                                               ctypes.byref(n)), "bmattn_forward_workspace_size")
+    return n.value
+
+
+def forward(q, k, v, desc: MaskDesc, tiles: BlockMask, *, block_table=None, scale: float = 0.0,
+            out=None, lse=None, workspace=None, with_lse: bool = True, stream=None):
+    """bmattn_forward.  q [total_q, H, D]; k, v [total_k, H, D] or page pools
+    [num_pages, page_size, H, D] with ``block_table`` [n_seqs, pages] int32.
+    Returns (O, LSE) with O like q and LSE fp32 [H, total_q]."""
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = forward_workspace_size(q, k, v, desc, tiles, block_table=block_table)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    a = _fwd_args(q, k, v, out, lse, block_table=block_table, scale=scale, workspace=workspace)
+    d, t = desc.c(), tiles.c()
+    _check(lib().bmattn_forward(ctypes.byref(a), ctypes.byref(d), ctypes.byref(t), _stream(stream)),
+           "bmattn_forward")
+    return out, lse
+
+
+def paged_gather(pool, block_table, desc: MaskDesc, stream=None):
+    """bmattn_paged_gather: pool [num_pages, page_size, H, D] -> [total_k, H, D]."""
+    n_pages, ps, H, D = pool.shape
+    out = torch.empty((desc.total_k, H, D), dtype=pool.dtype, device=pool.device)
+    d = desc.c()
+    _check(lib().bmattn_paged_gather(_ptr(pool), pool.stride(1), pool.stride(2), pool.element_size(),
+                                     H, D, ps, n_pages, _ptr(block_table), block_table.stride(0),
+                                     ctypes.byref(d), _ptr(out), _stream(stream)),
+           "bmattn_paged_gather")
+    return out
+
+
+def debug_dense_mask(desc: MaskDesc, tiles: BlockMask, seq: int, stream=None):
+    """bmattn_debug_dense_mask: uint8 [n_qt*block_m, n_kt*block_n] of one sequence."""
+    rows, cols = tiles.n_qt * tiles.block_m, tiles.n_kt * tiles.block_n
+    out = torch.empty((rows, cols), dtype=torch.uint8, device=tiles.tile_class.device)
+    d, t = desc.c(), tiles.c()
+    _check(lib().bmattn_debug_dense_mask(ctypes.byref(d), ctypes.byref(t), int(seq), _ptr(out), cols,
+                                         _stream(stream)), "bmattn_debug_dense_mask")
+    return out
+
+
+def validate(desc: MaskDesc, block_table=None, page_size: int = 0, num_pages: int = 0,
+             stream=None) -> int:
+    """bmattn_validate: returns the flag word (0 = valid); synchronises."""
+    flags = torch.zeros(1, dtype=torch.int32, device=desc.cu_seqlens_q.device)
+    d = desc.c()
+    _check(lib().bmattn_validate(ctypes.byref(d), _ptr(block_table),
+                                 0 if block_table is None else block_table.stride(0),
+                                 int(page_size), int(num_pages), _ptr(flags), _stream(stream)),
+           "bmattn_validate")
+    return int(flags.item())
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

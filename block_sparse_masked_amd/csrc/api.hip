@@ -1,0 +1,353 @@
+// C-ABI entry points of libbmattn: argument validation on the host, then the
+// launches.  No allocation, no state between calls (the last-error text is
+// thread-local), no exception crosses the boundary.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/bmattn.h"
+#include "launch.h"
+
+using namespace bmattn;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(BMATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Decode splits: consecutive entries of a row's kv-tile list per workgroup.
+constexpr int32_t kDecodeSplitTiles = 8;
+
+int check_desc(const bmattn_mask_desc* d) {
+  if (d == nullptr) return fail(BMATTN_EINVAL, "mask description is NULL");
+  if (d->kind < BMATTN_MASK_FULL || d->kind > BMATTN_MASK_STRIP_THINKING)
+    return fail(BMATTN_EINVAL, "unknown mask kind %d", d->kind);
+  if (d->n_seqs < 1) return fail(BMATTN_EINVAL, "n_seqs must be >= 1 (got %d)", d->n_seqs);
+  if (d->max_seqlen_q < 1 || d->max_seqlen_k < 1)
+    return fail(BMATTN_EINVAL, "max_seqlen_q/k must be >= 1 (got %d, %d)", d->max_seqlen_q,
+                d->max_seqlen_k);
+  if (d->total_q < 0 || d->total_k < 0) return fail(BMATTN_EINVAL, "negative total_q/total_k");
+  if (d->total_q > INT32_MAX || d->total_k > INT32_MAX)
+    return fail(BMATTN_EINVAL, "total_q/total_k exceed int32 (cu_seqlens are int32)");
+  if (d->cu_seqlens_q == nullptr || d->cu_seqlens_k == nullptr)
+    return fail(BMATTN_EINVAL, "cu_seqlens_q/k must be non-NULL");
+  if (d->kind == BMATTN_MASK_SHARED_PREFIX && (d->seg_q == nullptr || d->seg_k == nullptr))
+    return fail(BMATTN_EINVAL, "SHARED_PREFIX needs seg_q and seg_k");
+  if (d->kind == BMATTN_MASK_STRIP_THINKING &&
+      (d->role_k == nullptr || d->turn_q == nullptr || d->turn_k == nullptr))
+    return fail(BMATTN_EINVAL, "STRIP_THINKING needs role_k, turn_q and turn_k");
+  return BMATTN_OK;
+}
+
+MaskDev to_dev(const bmattn_mask_desc* d) {
+  MaskDev m{};
+  m.kind = d->kind;
+  m.n_seqs = d->n_seqs;
+  m.think_role = d->think_role;
+  m.total_q = d->total_q;
+  m.total_k = d->total_k;
+  m.cu_q = d->cu_seqlens_q;
+  m.cu_k = d->cu_seqlens_k;
+  m.seg_q = d->seg_q;
+  m.seg_k = d->seg_k;
+  m.role_k = d->role_k;
+  m.turn_q = d->turn_q;
+  m.turn_k = d->turn_k;
+  return m;
+}
+
+int shape(const bmattn_mask_desc* d, int32_t bm, int32_t bn, int32_t* n_qt, int32_t* n_kt,
+          int64_t* rows, int64_t* tiles) {
+  if (bm < 1 || bm > 1024 || bn < 1 || bn > 1024)
+    return fail(BMATTN_EUNSUPPORTED, "block_m/block_n must lie in [1, 1024] (got %d, %d)", bm, bn);
+  const int64_t qt = cdiv(d->max_seqlen_q, bm), kt = cdiv(d->max_seqlen_k, bn);
+  const int64_t r = qt * d->n_seqs;
+  if (r > INT32_MAX || r * kt > ((int64_t)1 << 40))
+    return fail(BMATTN_EINVAL, "block mask too large (%lld rows x %lld tiles)", (long long)r,
+                (long long)kt);
+  *n_qt = (int32_t)qt;
+  *n_kt = (int32_t)kt;
+  *rows = r;
+  *tiles = r * kt;
+  return BMATTN_OK;
+}
+
+int check_tiles(const bmattn_mask_desc* d, const bmattn_block_mask* t, bool need_write) {
+  if (t == nullptr) return fail(BMATTN_EINVAL, "block mask is NULL");
+  int32_t n_qt, n_kt;
+  int64_t rows, tiles;
+  int rc = shape(d, t->block_m, t->block_n, &n_qt, &n_kt, &rows, &tiles);
+  if (rc) return rc;
+  if (t->n_seqs != d->n_seqs || t->n_qt != n_qt || t->n_kt != n_kt)
+    return fail(BMATTN_EINVAL,
+                "block mask shape (n_seqs %d, n_qt %d, n_kt %d) does not match the description "
+                "(n_seqs %d, n_qt %d, n_kt %d)",
+                t->n_seqs, t->n_qt, t->n_kt, d->n_seqs, n_qt, n_kt);
+  if (t->full_cnt == nullptr || t->part_cnt == nullptr || t->full_idx == nullptr ||
+      t->part_idx == nullptr || t->row_order == nullptr || (need_write && t->tile_class == nullptr))
+    return fail(BMATTN_EINVAL, "block mask array is NULL");
+  return BMATTN_OK;
+}
+
+TilesDev tiles_dev(const bmattn_mask_desc* d, const bmattn_block_mask* t) {
+  TilesDev x{};
+  x.block_m = t->block_m;
+  x.block_n = t->block_n;
+  x.n_seqs = t->n_seqs;
+  x.n_qt = t->n_qt;
+  x.n_kt = t->n_kt;
+  x.max_lq = d->max_seqlen_q;
+  x.max_lk = d->max_seqlen_k;
+  x.tile_class = t->tile_class;
+  x.full_cnt = t->full_cnt;
+  x.part_cnt = t->part_cnt;
+  x.full_idx = t->full_idx;
+  x.part_idx = t->part_idx;
+  x.row_order = t->row_order;
+  return x;
+}
+
+enum class Path { kPrefill, kDecode, kNone };
+
+Path path_of(const bmattn_block_mask* t) {
+  if (t->block_m == 128 && t->block_n == 64) return Path::kPrefill;
+  if (t->block_m == 1 && t->block_n == 64) return Path::kDecode;
+  return Path::kNone;
+}
+
+size_t decode_workspace(const bmattn_fwd_args* a, const bmattn_block_mask* t) {
+  const int64_t rows = (int64_t)t->n_seqs * t->n_qt;
+  const int64_t splits = cdiv(t->n_kt, kDecodeSplitTiles);
+  return (size_t)(rows * splits * a->num_heads * (a->head_dim + 2)) * sizeof(float);
+}
+
+int check_fwd(const bmattn_fwd_args* a, const bmattn_mask_desc* d, const bmattn_block_mask* t) {
+  if (a == nullptr) return fail(BMATTN_EINVAL, "forward arguments are NULL");
+  int rc = check_desc(d);
+  if (rc) return rc;
+  rc = check_tiles(d, t, false);
+  if (rc) return rc;
+  if (a->dtype != BMATTN_F32 && a->dtype != BMATTN_BF16)
+    return fail(BMATTN_EUNSUPPORTED, "dtype %d is not compiled (F32 = 0, BF16 = 1)", a->dtype);
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(BMATTN_EUNSUPPORTED, "head_dim %d is not compiled (64 or 128)", a->head_dim);
+  if (a->num_heads < 1) return fail(BMATTN_EINVAL, "num_heads must be >= 1");
+  if (path_of(t) == Path::kNone)
+    return fail(BMATTN_EUNSUPPORTED,
+                "tile shape %dx%d is not compiled for the forward (128x64 or 1x64)", t->block_m,
+                t->block_n);
+  if (a->q == nullptr || a->k == nullptr || a->v == nullptr || a->o == nullptr)
+    return fail(BMATTN_EINVAL, "q, k, v and o must be non-NULL");
+  const int64_t eb = a->dtype == BMATTN_BF16 ? 2 : 4;
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->o))
+    return fail(BMATTN_EALIGN, "q, k, v and o must be 16-byte aligned");
+  const int64_t strides[8] = {a->q_stride_tok, a->q_stride_head, a->k_stride_tok, a->k_stride_head,
+                              a->v_stride_tok, a->v_stride_head, a->o_stride_tok, a->o_stride_head};
+  for (int i = 0; i < 8; ++i) {
+    if (strides[i] < 0) return fail(BMATTN_EINVAL, "negative stride");
+    if ((strides[i] * eb) % 16 != 0)
+      return fail(BMATTN_EALIGN, "token/head strides must be multiples of 16 bytes");
+  }
+  if (a->block_table != nullptr) {
+    if (a->page_size < 1) return fail(BMATTN_EINVAL, "page_size must be >= 1");
+    if (a->num_pages < 1) return fail(BMATTN_EINVAL, "num_pages must be >= 1");
+    if (a->block_table_stride < cdiv(d->max_seqlen_k, a->page_size))
+      return fail(BMATTN_EINVAL,
+                  "block_table_stride %lld is smaller than ceil(max_seqlen_k / page_size) = %lld",
+                  (long long)a->block_table_stride,
+                  (long long)cdiv(d->max_seqlen_k, a->page_size));
+  }
+  if (a->lse != nullptr && a->lse_stride_head < d->total_q)
+    return fail(BMATTN_EINVAL, "lse_stride_head must be >= total_q");
+  if (!(std::isfinite(a->scale)) || a->scale < 0.f)
+    return fail(BMATTN_EINVAL, "scale must be finite and >= 0 (0 selects 1/sqrt(head_dim))");
+  return BMATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bmattn_abi_version(void) { return BMATTN_ABI_VERSION; }
+
+const char* bmattn_last_error(void) { return g_last_error.c_str(); }
+
+const char* bmattn_status_string(int status) {
+  switch (status) {
+    case BMATTN_OK: return "ok";
+    case BMATTN_EINVAL: return "invalid argument";
+    case BMATTN_EUNSUPPORTED: return "unsupported configuration";
+    case BMATTN_EALIGN: return "misaligned pointer or stride";
+    case BMATTN_EHIP: return "HIP runtime error";
+    case BMATTN_EWORKSPACE: return "workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+int bmattn_block_mask_shape(const bmattn_mask_desc* desc, int32_t block_m, int32_t block_n,
+                            int32_t* n_qt, int32_t* n_kt, int64_t* rows, int64_t* tiles) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!n_qt || !n_kt || !rows || !tiles) return fail(BMATTN_EINVAL, "output pointer is NULL");
+  return shape(desc, block_m, block_n, n_qt, n_kt, rows, tiles);
+}
+
+int bmattn_build_block_mask(const bmattn_mask_desc* desc, const bmattn_block_mask* out,
+                            void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  rc = check_tiles(desc, out, true);
+  if (rc) return rc;
+  hipError_t e = launch_build_block_mask(to_dev(desc), tiles_dev(desc, out),
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bmattn_build_block_mask launch");
+  return BMATTN_OK;
+}
+
+int bmattn_forward_workspace_size(const bmattn_fwd_args* args, const bmattn_mask_desc* desc,
+                                  const bmattn_block_mask* tiles, size_t* bytes) {
+  if (bytes == nullptr) return fail(BMATTN_EINVAL, "bytes is NULL");
+  int rc = check_fwd(args, desc, tiles);
+  if (rc) return rc;
+  *bytes = path_of(tiles) == Path::kDecode ? decode_workspace(args, tiles) : 0;
+  return BMATTN_OK;
+}
+
+int bmattn_forward(const bmattn_fwd_args* a, const bmattn_mask_desc* desc,
+                   const bmattn_block_mask* t, void* stream) {
+  int rc = check_fwd(a, desc, t);
+  if (rc) return rc;
+  const Path path = path_of(t);
+  FwdDev p{};
+  p.mask = to_dev(desc);
+  p.block_m = t->block_m;
+  p.block_n = t->block_n;
+  p.n_qt = t->n_qt;
+  p.n_kt = t->n_kt;
+  p.max_lq = desc->max_seqlen_q;
+  p.max_lk = desc->max_seqlen_k;
+  p.full_cnt = t->full_cnt;
+  p.part_cnt = t->part_cnt;
+  p.full_idx = t->full_idx;
+  p.part_idx = t->part_idx;
+  p.row_order = t->row_order;
+  p.num_heads = a->num_heads;
+  p.head_dim = a->head_dim;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.o = a->o;
+  p.lse = a->lse;
+  p.q_st = a->q_stride_tok;
+  p.q_sh = a->q_stride_head;
+  p.k_st = a->k_stride_tok;
+  p.k_sh = a->k_stride_head;
+  p.v_st = a->v_stride_tok;
+  p.v_sh = a->v_stride_head;
+  p.o_st = a->o_stride_tok;
+  p.o_sh = a->o_stride_head;
+  p.lse_sh = a->lse_stride_head;
+  p.block_table = a->block_table;
+  p.bt_stride = a->block_table_stride;
+  p.num_pages = a->num_pages;
+  p.page_size = a->page_size;
+  const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->head_dim);
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const bool paged = a->block_table != nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (path == Path::kDecode) {
+    const size_t need = decode_workspace(a, t);
+    if (a->workspace == nullptr || a->workspace_bytes < need)
+      return fail(BMATTN_EWORKSPACE, "decode needs a workspace of %zu bytes (got %zu)", need,
+                  a->workspace == nullptr ? (size_t)0 : a->workspace_bytes);
+    if (!aligned16(a->workspace)) return fail(BMATTN_EALIGN, "workspace must be 16-byte aligned");
+    p.ws = static_cast<float*>(a->workspace);
+    p.split_tiles = kDecodeSplitTiles;
+    p.n_splits = (int32_t)cdiv(t->n_kt, kDecodeSplitTiles);
+    e = launch_forward_decode(p, a->dtype, paged, st);
+  } else {
+    e = launch_forward_prefill(p, a->dtype, paged, st);
+  }
+  if (e != hipSuccess) return hip_fail(e, "bmattn_forward launch");
+  return BMATTN_OK;
+}
+
+int bmattn_paged_gather(const void* pool, int64_t pool_stride_tok, int64_t pool_stride_head,
+                        int32_t elem_bytes, int32_t num_heads, int32_t head_dim,
+                        int32_t page_size, int64_t num_pages, const int32_t* block_table,
+                        int64_t block_table_stride, const bmattn_mask_desc* desc, void* out,
+                        void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (pool == nullptr || out == nullptr || block_table == nullptr)
+    return fail(BMATTN_EINVAL, "pool, block_table and out must be non-NULL");
+  if (elem_bytes != 2 && elem_bytes != 4) return fail(BMATTN_EINVAL, "elem_bytes must be 2 or 4");
+  if (num_heads < 1 || head_dim < 1) return fail(BMATTN_EINVAL, "num_heads/head_dim must be >= 1");
+  if ((head_dim * elem_bytes) % 16 != 0 || (pool_stride_tok * elem_bytes) % 16 != 0 ||
+      (pool_stride_head * elem_bytes) % 16 != 0 || !aligned16(pool) || !aligned16(out))
+    return fail(BMATTN_EALIGN, "rows, strides and pointers must be 16-byte aligned");
+  if (page_size < 1 || num_pages < 1) return fail(BMATTN_EINVAL, "page_size/num_pages must be >= 1");
+  if (block_table_stride < cdiv(desc->max_seqlen_k, page_size))
+    return fail(BMATTN_EINVAL, "block_table_stride smaller than ceil(max_seqlen_k / page_size)");
+  hipError_t e = launch_paged_gather(to_dev(desc), desc->max_seqlen_k, pool, pool_stride_tok,
+                                     pool_stride_head, elem_bytes, num_heads, head_dim, page_size,
+                                     num_pages, block_table, block_table_stride, out,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bmattn_paged_gather launch");
+  return BMATTN_OK;
+}
+
+int bmattn_debug_dense_mask(const bmattn_mask_desc* desc, const bmattn_block_mask* tiles,
+                            int32_t seq, uint8_t* out, int64_t out_stride, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  rc = check_tiles(desc, tiles, true);
+  if (rc) return rc;
+  if (seq < 0 || seq >= desc->n_seqs) return fail(BMATTN_EINVAL, "seq %d out of range", seq);
+  if (out == nullptr) return fail(BMATTN_EINVAL, "out is NULL");
+  if (out_stride < (int64_t)tiles->n_kt * tiles->block_n)
+    return fail(BMATTN_EINVAL, "out_stride must be >= n_kt * block_n");
+  hipError_t e = launch_debug_dense_mask(to_dev(desc), tiles_dev(desc, tiles), seq, out,
+                                         out_stride, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bmattn_debug_dense_mask launch");
+  return BMATTN_OK;
+}
+
+int bmattn_validate(const bmattn_mask_desc* desc, const int32_t* block_table,
+                    int64_t block_table_stride, int32_t page_size, int64_t num_pages,
+                    int32_t* flags, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (flags == nullptr) return fail(BMATTN_EINVAL, "flags is NULL");
+  if (block_table != nullptr && (page_size < 1 || num_pages < 1 || block_table_stride < 1))
+    return fail(BMATTN_EINVAL, "page_size, num_pages and block_table_stride must be >= 1");
+  hipError_t e = launch_validate(to_dev(desc), desc->max_seqlen_q, desc->max_seqlen_k, block_table,
+                                 block_table_stride, page_size, num_pages, flags,
+                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bmattn_validate launch");
+  return BMATTN_OK;
+}
+
+}  // extern "C"

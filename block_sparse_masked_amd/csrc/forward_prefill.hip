@@ -1,0 +1,426 @@
+// Block-sparse masked attention forward, query tiles of 128 rows (gfx950).
+//
+// Algorithm: Triton from First Principles, Ch. 21, section 21.1 -- the
+// online softmax over kv tiles with a running max m, a running sum l and an
+// accumulator rescaled by alpha = exp(m_old - m_new); section 21.2 -- the
+// element mask applied only where a tile straddles the mask boundary, and
+// tiles beyond it skipped.  Here the skip comes from the kv-tile lists of the
+// block mask: a workgroup walks its row's FULL tiles (no mask code) and then
+// its PARTIAL tiles (element predicate); EMPTY tiles are never loaded.
+//
+// Mapping onto CDNA4 (not the pages' design):
+//  * one workgroup = 4 waves = 128 query rows of one (sequence, head); each
+//    wave owns 32 query rows for the whole kv loop;
+//  * a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K tile
+//    rows from LDS, B = the wave's Q rows held in registers), so lane l holds
+//    the scores of query (l % 32) against 16 keys per 32-key block.  The row
+//    max and row sum are then lane-local plus one exchange with lane l ^ 32;
+//  * the A operand rows are permuted (bits 2 and 3 of the row index
+//    swapped) so that each lane's 8 consecutive accumulator registers hold 8
+//    consecutive keys: the probabilities feed the P V product as the B
+//    operand directly from registers, with V^T read from LDS;
+//  * K and V^T tiles (BLOCK_N = 64 keys) are double-buffered in LDS and the
+//    next tile's global loads are in flight while the current one is used;
+//  * exponentials are base 2 with log2(e) folded into the softmax scale.
+// The fp32 variant uses v_mfma_f32_32x32x2_f32 with the same accumulator
+// layout.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace bmattn {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kBM = 128;
+constexpr int kBN = 64;
+constexpr int kThreads = 256;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+template <typename T, int D>
+struct Cfg {
+  static constexpr int kElem = sizeof(T);
+  static constexpr int kRowB = D * kElem;           // bytes of one K/V row
+  static constexpr int kCh = kRowB / 16;             // 16-byte chunks per row
+  static constexpr int kEpc = 16 / kElem;            // elements per chunk
+  static constexpr int kKP = kRowB + 16;             // K row pitch in LDS (bytes)
+  static constexpr int kVP = kBN * kElem + 16;       // V^T row pitch in LDS (bytes)
+  static constexpr int kKBuf = kBN * kKP;
+  static constexpr int kVBuf = D * kVP;
+  static constexpr int kStage = kKBuf + kVBuf;
+  static constexpr int kKChunks = kBN * kCh / kThreads;  // K chunks per thread
+  static constexpr int kKpt = kBN * kCh / kThreads;      // keys per thread (V staging)
+  static constexpr int kDT = D / 32;                     // 32-wide output d tiles
+  static_assert(kKChunks * kThreads == kBN * kCh, "tile / thread mismatch");
+};
+
+__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Row index permutation of the 32-row MFMA operand: swaps bits 2 and 3.
+__device__ __forceinline__ int sigma(int i) {
+  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = static_cast<__bf16>(lo);
+  __bf16 b = static_cast<__bf16>(hi);
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+template <typename T, int D, bool PAGED>
+struct Prefill {
+  using C = Cfg<T, D>;
+
+  // Global address (bytes) of key row j of sequence s for head h.
+  static __device__ __forceinline__ const char* krow(const FwdDev& p, const char* base,
+                                                      int64_t st_tok, int64_t st_head,
+                                                      const SeqBounds& sb, int s, int h, int j) {
+    int64_t r = PAGED ? paged_row(p.block_table, p.bt_stride, s, j, p.page_size, p.num_pages)
+                      : sb.k0 + j;
+    return base + (r * st_tok + (int64_t)h * st_head) * C::kElem;
+  }
+
+  // Global -> registers for one kv tile.  Rows past the sequence (only in
+  // PARTIAL tiles) are zero and never read.
+  static __device__ __forceinline__ void load_tile(const FwdDev& p, const SeqBounds& sb, int s,
+                                                   int h, int kt, bool masked, int tid,
+                                                   uint4 (&kr)[C::kKChunks],
+                                                   uint4 (&vr)[C::kKpt]) {
+    const char* kb = static_cast<const char*>(p.k);
+    const char* vb = static_cast<const char*>(p.v);
+#pragma unroll
+    for (int u = 0; u < C::kKChunks; ++u) {
+      const int c = tid + kThreads * u;
+      const int row = c / C::kCh, ch = c % C::kCh;
+      const int j = kt * kBN + row;
+      if (!masked || j < sb.lk) {
+        kr[u] = *reinterpret_cast<const uint4*>(krow(p, kb, p.k_st, p.k_sh, sb, s, h, j) + ch * 16);
+      } else {
+        kr[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    const int ch = tid % C::kCh, kg = tid / C::kCh;
+#pragma unroll
+    for (int u = 0; u < C::kKpt; ++u) {
+      const int j = kt * kBN + kg * C::kKpt + u;
+      if (!masked || j < sb.lk) {
+        vr[u] = *reinterpret_cast<const uint4*>(krow(p, vb, p.v_st, p.v_sh, sb, s, h, j) + ch * 16);
+      } else {
+        vr[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+
+  // Registers -> LDS: K row-major, V transposed (V^T[d][key]).
+  static __device__ __forceinline__ void store_tile(char* stage, int tid,
+                                                    const uint4 (&kr)[C::kKChunks],
+                                                    const uint4 (&vr)[C::kKpt]) {
+#pragma unroll
+    for (int u = 0; u < C::kKChunks; ++u) {
+      const int c = tid + kThreads * u;
+      const int row = c / C::kCh, ch = c % C::kCh;
+      *reinterpret_cast<uint4*>(stage + row * C::kKP + ch * 16) = kr[u];
+    }
+    char* vt = stage + C::kKBuf;
+    const int ch = tid % C::kCh, kg = tid / C::kCh;
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t* w[C::kKpt];
+#pragma unroll
+      for (int u = 0; u < C::kKpt; ++u) w[u] = reinterpret_cast<const uint32_t*>(&vr[u]);
+#pragma unroll
+      for (int e = 0; e < C::kEpc; ++e) {
+        const int d = ch * C::kEpc + e;
+        const int sh = (e & 1) * 16;
+        uint32_t h16[C::kKpt];
+#pragma unroll
+        for (int u = 0; u < C::kKpt; ++u) h16[u] = (w[u][e >> 1] >> sh) & 0xffffu;
+        char* dst = vt + d * C::kVP + kg * C::kKpt * 2;
+        if constexpr (C::kKpt == 4) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16));
+        } else {
+          *reinterpret_cast<uint32_t*>(dst) = h16[0] | (h16[1] << 16);
+        }
+      }
+    } else {
+      static_assert(C::kKpt == 4 || C::kKpt == 8, "fp32 staging expects 4 or 8 keys per thread");
+#pragma unroll
+      for (int e = 0; e < C::kEpc; ++e) {
+        const int d = ch * C::kEpc + e;
+        char* dst = vt + d * C::kVP + kg * C::kKpt * 4;
+#pragma unroll
+        for (int u0 = 0; u0 < C::kKpt; u0 += 4) {
+          const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vr[u0 + 0]);
+          const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vr[u0 + 1]);
+          const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vr[u0 + 2]);
+          const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vr[u0 + 3]);
+          *reinterpret_cast<uint4*>(dst + u0 * 4) = make_uint4(w0[e], w1[e], w2[e], w3[e]);
+        }
+      }
+    }
+  }
+};
+
+// Q operand of one lane: bf16 -> 8 values per 16-wide k step; fp32 -> one
+// value per 2-wide k step, lane group g taking d in [g*D/2, g*D/2 + D/2).
+template <typename T, int D>
+struct QFrag;
+template <int D>
+struct QFrag<__bf16, D> {
+  bf16x8 v[D / 16];
+};
+template <int D>
+struct QFrag<float, D> {
+  float v[D / 2];
+};
+
+template <typename T, int D, bool PAGED>
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(FwdDev p) {
+  using C = Cfg<T, D>;
+  using P = Prefill<T, D, PAGED>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::kStage];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  const uint32_t n_rows = (uint32_t)p.mask.n_seqs * p.n_qt;
+  const uint32_t w = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = (int)(w / n_rows);
+  const int row = p.row_order[w % n_rows];
+  const int s = row / p.n_qt, a = row % p.n_qt;
+  const SeqBounds sb = seq_bounds(p.mask, s, p.max_lq, p.max_lk);
+  if (a * kBM >= sb.lq) return;
+  const int nfull = p.full_cnt[row];
+  const int ntiles = nfull + p.part_cnt[row];
+  const int32_t* flist = p.full_idx + (int64_t)row * p.n_kt;
+  const int32_t* plist = p.part_idx + (int64_t)row * p.n_kt;
+
+  const int qi = a * kBM + wave * 32 + l32;  // query row inside the sequence
+  const bool qvalid = qi < sb.lq;
+  const QIds qids = load_qids(p.mask, sb, qi);
+
+  // Q operand (B of S^T = K Q^T), resident for the whole kv loop.
+  QFrag<T, D> qf;
+  {
+    const char* qrow = static_cast<const char*>(p.q) +
+                       ((sb.q0 + (qvalid ? qi : 0)) * p.q_st + (int64_t)h * p.q_sh) * C::kElem;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        uint4 x = qvalid ? *reinterpret_cast<const uint4*>(qrow + (ks * 16 + g * 8) * 2)
+                         : make_uint4(0, 0, 0, 0);
+        qf.v[ks] = __builtin_bit_cast(bf16x8, x);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) {
+        float4 x = qvalid ? *reinterpret_cast<const float4*>(qrow + (g * (D / 2) + c * 4) * 4)
+                          : make_float4(0, 0, 0, 0);
+        qf.v[c * 4 + 0] = x.x;
+        qf.v[c * 4 + 1] = x.y;
+        qf.v[c * 4 + 2] = x.z;
+        qf.v[c * 4 + 3] = x.w;
+      }
+    }
+  }
+
+  f32x16 acc[C::kDT];
+#pragma unroll
+  for (int dt = 0; dt < C::kDT; ++dt) acc[dt] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = p.scale_log2;
+  const int krow_a = sigma(l32);
+
+  uint4 kr[C::kKChunks];
+  uint4 vr[C::kKpt];
+  if (ntiles > 0) {
+    const int kt0 = nfull > 0 ? flist[0] : plist[0];
+    P::load_tile(p, sb, s, h, kt0, nfull == 0, tid, kr, vr);
+    P::store_tile(smem, tid, kr, vr);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const bool masked = t >= nfull;
+    const int kt = masked ? plist[t - nfull] : flist[t];
+    const bool has_next = t + 1 < ntiles;
+    if (has_next) {
+      const bool mnext = t + 1 >= nfull;
+      const int ktn = mnext ? plist[t + 1 - nfull] : flist[t + 1];
+      P::load_tile(p, sb, s, h, ktn, mnext, tid, kr, vr);
+    }
+    const char* Ks = smem + (t & 1) * C::kStage;
+    const char* Vt = Ks + C::kKBuf;
+
+    // ---- S^T = K Q^T for the two 32-key blocks of the tile -------------
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(Ks + krow_a * C::kKP + (ks * 16 + g * 8) * 2);
+        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(Ks + (32 + krow_a) * C::kKP + (ks * 16 + g * 8) * 2);
+        s0 = mfma(k0, qf.v[ks], s0);
+        s1 = mfma(k1, qf.v[ks], s1);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < D / 8; ++c) {
+        const float4 k0 = *reinterpret_cast<const float4*>(Ks + krow_a * C::kKP + (g * (D / 2) + c * 4) * 4);
+        const float4 k1 = *reinterpret_cast<const float4*>(Ks + (32 + krow_a) * C::kKP + (g * (D / 2) + c * 4) * 4);
+        s0 = mfma(k0.x, qf.v[c * 4 + 0], s0);
+        s1 = mfma(k1.x, qf.v[c * 4 + 0], s1);
+        s0 = mfma(k0.y, qf.v[c * 4 + 1], s0);
+        s1 = mfma(k1.y, qf.v[c * 4 + 1], s1);
+        s0 = mfma(k0.z, qf.v[c * 4 + 2], s0);
+        s1 = mfma(k1.z, qf.v[c * 4 + 2], s1);
+        s0 = mfma(k0.w, qf.v[c * 4 + 3], s0);
+        s1 = mfma(k1.w, qf.v[c * 4 + 3], s1);
+      }
+    }
+
+    // ---- online softmax (base 2) ---------------------------------------
+    // Register r of block b holds key kt*64 + b*32 + 16*(r/8) + 8*g + r%8.
+    float x[32];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      x[r] = s0[r] * sl2;
+      x[16 + r] = s1[r] * sl2;
+    }
+    if (masked) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = kt * kBN + b * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
+          if (!visible(p.mask, sb, qi, qids, j)) x[b * 16 + r] = -INFINITY;
+        }
+      }
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int r = 1; r < 32; ++r) mx = fmaxf(mx, x[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      x[r] = fast_exp2(x[r] - m_use);
+      rs += x[r];
+    }
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < C::kDT; ++dt) acc[dt] *= alpha;
+    }
+
+    // ---- acc^T += V^T P^T ------------------------------------------------
+    if constexpr (sizeof(T) == 2) {
+      bf16x8 pf[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint4 u;
+        u.x = pack_bf16x2(x[k * 8 + 0], x[k * 8 + 1]);
+        u.y = pack_bf16x2(x[k * 8 + 2], x[k * 8 + 3]);
+        u.z = pack_bf16x2(x[k * 8 + 4], x[k * 8 + 5]);
+        u.w = pack_bf16x2(x[k * 8 + 6], x[k * 8 + 7]);
+        pf[k] = __builtin_bit_cast(bf16x8, u);
+      }
+#pragma unroll
+      for (int dt = 0; dt < C::kDT; ++dt) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + (dt * 32 + l32) * C::kVP + (k * 16 + g * 8) * 2);
+          acc[dt] = mfma(vf, pf[k], acc[dt]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < C::kDT; ++dt) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const char* src = Vt + (dt * 32 + l32) * C::kVP + (b * 32 + 16 * hh + 8 * g) * 4;
+            const float4 v0 = *reinterpret_cast<const float4*>(src);
+            const float4 v1 = *reinterpret_cast<const float4*>(src + 16);
+            const int r0 = b * 16 + hh * 8;
+            acc[dt] = mfma(v0.x, x[r0 + 0], acc[dt]);
+            acc[dt] = mfma(v0.y, x[r0 + 1], acc[dt]);
+            acc[dt] = mfma(v0.z, x[r0 + 2], acc[dt]);
+            acc[dt] = mfma(v0.w, x[r0 + 3], acc[dt]);
+            acc[dt] = mfma(v1.x, x[r0 + 4], acc[dt]);
+            acc[dt] = mfma(v1.y, x[r0 + 5], acc[dt]);
+            acc[dt] = mfma(v1.z, x[r0 + 6], acc[dt]);
+            acc[dt] = mfma(v1.w, x[r0 + 7], acc[dt]);
+          }
+        }
+      }
+    }
+
+    if (has_next) P::store_tile(smem + ((t + 1) & 1) * C::kStage, tid, kr, vr);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l, LSE = m + ln(l) ------------------------------
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qvalid) {
+    char* orow = static_cast<char*>(p.o) + ((sb.q0 + qi) * p.o_st + (int64_t)h * p.o_sh) * C::kElem;
+#pragma unroll
+    for (int dt = 0; dt < C::kDT; ++dt) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d0 = dt * 32 + 8 * a4 + 4 * g;
+        const float o0 = acc[dt][a4 * 4 + 0] * inv, o1 = acc[dt][a4 * 4 + 1] * inv;
+        const float o2 = acc[dt][a4 * 4 + 2] * inv, o3 = acc[dt][a4 * 4 + 3] * inv;
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<uint2*>(orow + d0 * 2) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+        } else {
+          *reinterpret_cast<float4*>(orow + d0 * 4) = make_float4(o0, o1, o2, o3);
+        }
+      }
+    }
+    if (g == 0 && p.lse != nullptr) {
+      const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      p.lse[(int64_t)h * p.lse_sh + sb.q0 + qi] = lse;
+    }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const FwdDev& p, bool paged, hipStream_t st) {
+  const uint32_t n_rows = (uint32_t)p.mask.n_seqs * p.n_qt;
+  const uint32_t grid = n_rows * (uint32_t)p.num_heads;
+  if (grid == 0) return hipSuccess;
+  if (paged) {
+    hipLaunchKernelGGL((prefill_kernel<T, D, true>), dim3(grid), dim3(kThreads), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<T, D, false>), dim3(grid), dim3(kThreads), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_forward_prefill(const FwdDev& p, int dtype, bool paged, hipStream_t st) {
+  if (p.block_m != kBM || p.block_n != kBN) return hipErrorInvalidValue;
+  if (dtype == BMATTN_BF16 && p.head_dim == 128) return launch_typed<__bf16, 128>(p, paged, st);
+  if (dtype == BMATTN_BF16 && p.head_dim == 64) return launch_typed<__bf16, 64>(p, paged, st);
+  if (dtype == BMATTN_F32 && p.head_dim == 128) return launch_typed<float, 128>(p, paged, st);
+  if (dtype == BMATTN_F32 && p.head_dim == 64) return launch_typed<float, 64>(p, paged, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace bmattn

@@ -1,0 +1,68 @@
+// Internal host-side launchers (not part of the C ABI).  Each .hip file
+// defines its kernels and the launcher that configures them; api.cpp
+// validates arguments and calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+
+namespace bmattn {
+
+struct TilesDev {
+  int32_t block_m, block_n, n_seqs, n_qt, n_kt;
+  int32_t max_lq, max_lk;
+  uint8_t* tile_class;
+  int32_t* full_cnt;
+  int32_t* part_cnt;
+  int32_t* full_idx;
+  int32_t* part_idx;
+  int32_t* row_order;
+};
+
+// Common forward parameters for the kernels.
+struct FwdDev {
+  MaskDev mask;
+  // read-only view of the tiles
+  int32_t block_m, block_n, n_qt, n_kt;
+  int32_t max_lq, max_lk;
+  const int32_t* full_cnt;
+  const int32_t* part_cnt;
+  const int32_t* full_idx;
+  const int32_t* part_idx;
+  const int32_t* row_order;
+  int32_t num_heads, head_dim;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh, lse_sh;
+  const int32_t* block_table;
+  int64_t bt_stride, num_pages;
+  int32_t page_size;
+  float scale_log2;  // softmax scale times log2(e)
+  // decode split-KV
+  float* ws;             // [n_rows, splits, H, D + 2] partial results
+  int32_t split_tiles;   // kv tiles per split
+  int32_t n_splits;      // splits per row
+};
+
+hipError_t launch_build_block_mask(const MaskDev& m, const TilesDev& t, hipStream_t st);
+hipError_t launch_debug_dense_mask(const MaskDev& m, const TilesDev& t, int seq, uint8_t* out,
+                                   int64_t out_stride, hipStream_t st);
+hipError_t launch_validate(const MaskDev& m, int32_t max_lq, int32_t max_lk,
+                           const int32_t* block_table, int64_t bt_stride, int32_t page_size,
+                           int64_t num_pages, int32_t* flags, hipStream_t st);
+hipError_t launch_paged_gather(const MaskDev& m, int32_t max_lk, const void* pool, int64_t st_tok,
+                               int64_t st_head, int32_t elem_bytes, int32_t H, int32_t D,
+                               int32_t page_size, int64_t num_pages, const int32_t* block_table,
+                               int64_t bt_stride, void* out, hipStream_t st);
+
+// Forward kernels.  Return hipErrorInvalidValue for a combination that is
+// not compiled (the caller checks support first).
+hipError_t launch_forward_prefill(const FwdDev& p, int dtype, bool paged, hipStream_t st);
+hipError_t launch_forward_decode(const FwdDev& p, int dtype, bool paged, hipStream_t st);
+
+}  // namespace bmattn

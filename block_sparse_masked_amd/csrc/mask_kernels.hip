@@ -1,0 +1,310 @@
+// Tile classification, kv-tile lists, row schedule, dense-mask export,
+// device-side validation and the paged gather export.
+//
+// Tile classes follow the tiled causal diagram of Triton from First
+// Principles, Ch. 21, section 21.2 (all-valid blocks, the diagonal block
+// checked per pair, blocks skipped without a load) with pairs outside the
+// sequence counted as not visible.  The lists let a forward workgroup skip
+// every empty tile on a scalar read, as in Ch. 9, section 9.2.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace bmattn {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxBlock = 1024;
+
+// Visible query rows of a tile for key j when every pair of the tile passes
+// the causal condition and lies inside the sequence.  qid holds the row ids
+// (segment or turn) of the tile's query rows, [qmin, qmax] their range.
+__device__ __forceinline__ int key_visible_rows(const MaskDev& m, const SeqBounds& b, int j,
+                                                const int32_t* qid, int nrows, int32_t qmin,
+                                                int32_t qmax) {
+  if (m.kind == BMATTN_MASK_SHARED_PREFIX) {
+    int32_t sk = m.seg_k[b.k0 + j];
+    if (sk == 0) return nrows;
+    if (sk < qmin || sk > qmax) return 0;
+    if (qmin == qmax) return nrows;
+    int c = 0;
+    for (int i = 0; i < nrows; ++i) c += (qid[i] == sk);
+    return c;
+  }
+  // STRIP_THINKING: hidden when the key is think and from an earlier turn.
+  if (m.role_k[b.k0 + j] != m.think_role) return nrows;
+  int32_t tk = m.turn_k[b.k0 + j];
+  if (tk >= qmax) return nrows;
+  if (tk < qmin) return 0;
+  int c = 0;
+  for (int i = 0; i < nrows; ++i) c += (tk >= qid[i]);
+  return c;
+}
+
+__device__ uint8_t classify_tile(const MaskDev& m, const SeqBounds& b, int qlo, int klo, int BM,
+                                 int BN, const int32_t* qid, int32_t qmin, int32_t qmax) {
+  if (qlo >= b.lq || klo >= b.lk) return BMATTN_TILE_EMPTY;
+  const int qhi = min(qlo + BM, b.lq);
+  const int khi = min(klo + BN, b.lk);
+  const bool inside = (qlo + BM <= b.lq) && (klo + BN <= b.lk);
+  if (m.kind == BMATTN_MASK_FULL) return inside ? BMATTN_TILE_FULL : BMATTN_TILE_PARTIAL;
+  const int64_t off = (int64_t)b.lk - b.lq;
+  // Every key beyond the last query's position: nothing visible.
+  if ((int64_t)klo > (int64_t)(qhi - 1) + off) return BMATTN_TILE_EMPTY;
+  const bool causal_full = inside && ((int64_t)klo + BN - 1 <= (int64_t)qlo + off);
+  if (m.kind == BMATTN_MASK_CAUSAL)
+    return causal_full ? BMATTN_TILE_FULL : BMATTN_TILE_PARTIAL;
+  if (causal_full) {
+    // Only the id condition can hide pairs: count visible rows key by key.
+    int64_t nvis = 0;
+    bool hidden = false;
+    for (int j = klo; j < khi; ++j) {
+      int c = key_visible_rows(m, b, j, qid, BM, qmin, qmax);
+      nvis += c;
+      hidden |= (c < BM);
+      if (nvis > 0 && hidden) return BMATTN_TILE_PARTIAL;
+    }
+    if (nvis == 0) return BMATTN_TILE_EMPTY;
+    return hidden ? BMATTN_TILE_PARTIAL : BMATTN_TILE_FULL;
+  }
+  // Diagonal or edge tile: enumerate the pairs (out-of-range pairs hidden).
+  bool any_vis = false, any_hid = !inside;
+  for (int j = klo; j < khi; ++j) {
+    for (int i = qlo; i < qhi; ++i) {
+      QIds q{qid[i - qlo], qid[i - qlo]};
+      bool v = visible(m, b, i, q, j);
+      any_vis |= v;
+      any_hid |= !v;
+      if (any_vis && any_hid) return BMATTN_TILE_PARTIAL;
+    }
+  }
+  if (!any_vis) return BMATTN_TILE_EMPTY;
+  return any_hid ? BMATTN_TILE_PARTIAL : BMATTN_TILE_FULL;
+}
+
+// One workgroup per query-tile row: classifies the row's kv tiles in chunks
+// of 256 and appends FULL / PARTIAL indices in ascending order.
+__global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev t) {
+  __shared__ int32_t qid[kMaxBlock];
+  __shared__ int32_t wave_tot[2][kThreads / 64];
+  __shared__ int32_t red[2][kThreads / 64];
+  const int row = blockIdx.x;
+  const int s = row / t.n_qt, a = row % t.n_qt;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int BM = t.block_m, BN = t.block_n;
+  const SeqBounds b = seq_bounds(m, s, t.max_lq, t.max_lk);
+  const int qlo = a * BM;
+
+  // Row ids (segment for shared-prefix, turn for strip-thinking) and range.
+  int32_t lmin = INT32_MAX, lmax = INT32_MIN;
+  for (int i = tid; i < BM; i += kThreads) {
+    QIds x = load_qids(m, b, qlo + i);
+    int32_t v = (m.kind == BMATTN_MASK_SHARED_PREFIX) ? x.seg : x.turn;
+    qid[i] = v;
+    if (qlo + i < b.lq) {
+      lmin = min(lmin, v);
+      lmax = max(lmax, v);
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    lmin = min(lmin, __shfl_xor(lmin, o));
+    lmax = max(lmax, __shfl_xor(lmax, o));
+  }
+  if (lane == 0) {
+    red[0][wave] = lmin;
+    red[1][wave] = lmax;
+  }
+  __syncthreads();
+  int32_t qmin = red[0][0], qmax = red[1][0];
+  for (int w = 1; w < kThreads / 64; ++w) {
+    qmin = min(qmin, red[0][w]);
+    qmax = max(qmax, red[1][w]);
+  }
+
+  const int64_t rowoff = (int64_t)row * t.n_kt;
+  int full_base = 0, part_base = 0;
+  for (int c0 = 0; c0 < t.n_kt; c0 += kThreads) {
+    const int bidx = c0 + tid;
+    uint8_t cls = BMATTN_TILE_EMPTY;
+    if (bidx < t.n_kt) {
+      cls = classify_tile(m, b, qlo, bidx * BN, BM, BN, qid, qmin, qmax);
+      t.tile_class[rowoff + bidx] = cls;
+    }
+    const uint64_t fm = __ballot(cls == BMATTN_TILE_FULL);
+    const uint64_t pm = __ballot(cls == BMATTN_TILE_PARTIAL);
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int frank = __popcll(fm & lt), prank = __popcll(pm & lt);
+    if (lane == 0) {
+      wave_tot[0][wave] = __popcll(fm);
+      wave_tot[1][wave] = __popcll(pm);
+    }
+    __syncthreads();
+    int fo = full_base, po = part_base, ft = 0, pt = 0;
+    for (int w = 0; w < kThreads / 64; ++w) {
+      if (w < wave) {
+        fo += wave_tot[0][w];
+        po += wave_tot[1][w];
+      }
+      ft += wave_tot[0][w];
+      pt += wave_tot[1][w];
+    }
+    if (cls == BMATTN_TILE_FULL) t.full_idx[rowoff + fo + frank] = bidx;
+    if (cls == BMATTN_TILE_PARTIAL) t.part_idx[rowoff + po + prank] = bidx;
+    full_base += ft;
+    part_base += pt;
+    __syncthreads();
+  }
+  for (int i = full_base + tid; i < t.n_kt; i += kThreads) t.full_idx[rowoff + i] = -1;
+  for (int i = part_base + tid; i < t.n_kt; i += kThreads) t.part_idx[rowoff + i] = -1;
+  if (tid == 0) {
+    t.full_cnt[row] = full_base;
+    t.part_cnt[row] = part_base;
+  }
+}
+
+// Rows sorted by descending listed-tile count (ties: ascending row), so the
+// longest rows are dispatched first.  Rank of row r = number of rows that
+// sort before it; the keys are distinct, so the ranks are a permutation.
+__global__ __launch_bounds__(kThreads) void schedule_kernel(TilesDev t, int rows) {
+  __shared__ int32_t wsh[kThreads];
+  const int r = blockIdx.x * kThreads + threadIdx.x;
+  const int my = r < rows ? t.full_cnt[r] + t.part_cnt[r] : 0;
+  int rank = 0;
+  for (int c0 = 0; c0 < rows; c0 += kThreads) {
+    const int idx = c0 + threadIdx.x;
+    wsh[threadIdx.x] = idx < rows ? t.full_cnt[idx] + t.part_cnt[idx] : -1;
+    __syncthreads();
+    const int lim = min(kThreads, rows - c0);
+    for (int k = 0; k < lim; ++k) {
+      const int w = wsh[k];
+      rank += (w > my) || (w == my && c0 + k < r);
+    }
+    __syncthreads();
+  }
+  if (r < rows) t.row_order[rank] = r;
+}
+
+__global__ __launch_bounds__(kThreads) void dense_mask_kernel(MaskDev m, TilesDev t, int seq,
+                                                              uint8_t* out, int64_t stride) {
+  const int64_t rows_out = (int64_t)t.n_qt * t.block_m;
+  const int64_t cols_out = (int64_t)t.n_kt * t.block_n;
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= rows_out * cols_out) return;
+  const int i = (int)(idx / cols_out), j = (int)(idx % cols_out);
+  const SeqBounds b = seq_bounds(m, seq, t.max_lq, t.max_lk);
+  const int a = i / t.block_m, bb = j / t.block_n;
+  const uint8_t cls = t.tile_class[((int64_t)seq * t.n_qt + a) * t.n_kt + bb];
+  uint8_t v = 0;
+  if (cls == BMATTN_TILE_FULL) {
+    v = 1;
+  } else if (cls == BMATTN_TILE_PARTIAL) {
+    v = visible(m, b, i, load_qids(m, b, i), j) ? 1 : 0;
+  }
+  out[(int64_t)i * stride + j] = v;
+}
+
+__global__ __launch_bounds__(kThreads) void validate_kernel(MaskDev m, int32_t max_lq,
+                                                            int32_t max_lk, const int32_t* bt,
+                                                            int64_t bt_stride, int32_t page_size,
+                                                            int64_t num_pages, int32_t* flags) {
+  int f = 0;
+  if (threadIdx.x == 0) {
+    if (m.cu_q[0] != 0 || (int64_t)m.cu_q[m.n_seqs] != m.total_q) f |= 1;
+    if (m.cu_k[0] != 0 || (int64_t)m.cu_k[m.n_seqs] != m.total_k) f |= 2;
+  }
+  for (int s = threadIdx.x; s < m.n_seqs; s += kThreads) {
+    const int32_t lq = m.cu_q[s + 1] - m.cu_q[s];
+    const int32_t lk = m.cu_k[s + 1] - m.cu_k[s];
+    if (lq < 0) f |= 1;
+    if (lk < 0) f |= 2;
+    if (lq > max_lq || lk > max_lk) f |= 4;
+    if (bt != nullptr && lk > 0) {
+      const int64_t pages = ((int64_t)lk + page_size - 1) / page_size;
+      if (pages > bt_stride) {
+        f |= 8;
+      } else {
+        for (int64_t p = 0; p < pages; ++p) {
+          const int32_t e = bt[(int64_t)s * bt_stride + p];
+          if (e < 0 || e >= num_pages) f |= 8;
+        }
+      }
+    }
+  }
+  // OR-reduce over the workgroup.
+  __shared__ int32_t red[kThreads / 64];
+  for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = f;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int tot = 0;
+    for (int w = 0; w < kThreads / 64; ++w) tot |= red[w];
+    flags[0] = tot;
+  }
+}
+
+// Copies 16-byte chunks of every (key, head) row from the pool to the
+// contiguous output through paged_row, the forward's own addressing.
+__global__ __launch_bounds__(kThreads) void paged_gather_kernel(
+    MaskDev m, int32_t max_lk, const char* pool, int64_t st_tok_b, int64_t st_head_b, int32_t H,
+    int32_t row_bytes, int32_t page_size, int64_t num_pages, const int32_t* bt, int64_t bt_stride,
+    char* out) {
+  const int s = blockIdx.y;
+  const int chunks = row_bytes / 16;
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t per_tok = (int64_t)H * chunks;
+  const int j = (int)(idx / per_tok);
+  const int rem = (int)(idx % per_tok);
+  const int h = rem / chunks, c = rem % chunks;
+  const SeqBounds b = seq_bounds(m, s, 1 << 30, max_lk);
+  if (j >= b.lk) return;  // the ragged tail is masked: no read, no write
+  const int64_t prow = paged_row(bt, bt_stride, s, j, page_size, num_pages);
+  const uint4 v = *reinterpret_cast<const uint4*>(pool + prow * st_tok_b + h * st_head_b + c * 16);
+  *reinterpret_cast<uint4*>(out + ((b.k0 + j) * H + h) * (int64_t)row_bytes + c * 16) = v;
+}
+
+}  // namespace
+
+hipError_t launch_build_block_mask(const MaskDev& m, const TilesDev& t, hipStream_t st) {
+  const int rows = t.n_seqs * t.n_qt;
+  hipLaunchKernelGGL(classify_kernel, dim3(rows), dim3(kThreads), 0, st, m, t);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(schedule_kernel, dim3((rows + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                     st, t, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_dense_mask(const MaskDev& m, const TilesDev& t, int seq, uint8_t* out,
+                                   int64_t out_stride, hipStream_t st) {
+  const int64_t n = (int64_t)t.n_qt * t.block_m * t.n_kt * t.block_n;
+  const int64_t blocks = (n + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(dense_mask_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, st, m, t, seq,
+                     out, out_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_validate(const MaskDev& m, int32_t max_lq, int32_t max_lk,
+                           const int32_t* block_table, int64_t bt_stride, int32_t page_size,
+                           int64_t num_pages, int32_t* flags, hipStream_t st) {
+  hipLaunchKernelGGL(validate_kernel, dim3(1), dim3(kThreads), 0, st, m, max_lq, max_lk,
+                     block_table, bt_stride, page_size, num_pages, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_paged_gather(const MaskDev& m, int32_t max_lk, const void* pool, int64_t st_tok,
+                               int64_t st_head, int32_t elem_bytes, int32_t H, int32_t D,
+                               int32_t page_size, int64_t num_pages, const int32_t* block_table,
+                               int64_t bt_stride, void* out, hipStream_t st) {
+  const int32_t row_bytes = D * elem_bytes;
+  const int64_t n = (int64_t)max_lk * H * (row_bytes / 16);
+  const int64_t blocks = (n + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(paged_gather_kernel, dim3((uint32_t)blocks, m.n_seqs), dim3(kThreads), 0, st,
+                     m, max_lk, static_cast<const char*>(pool), st_tok * elem_bytes,
+                     st_head * elem_bytes, H, row_bytes, page_size, num_pages, block_table,
+                     bt_stride, static_cast<char*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace bmattn

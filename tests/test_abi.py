@@ -1,0 +1,179 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/bmattn.h declares, and rejects invalid calls on the host before any
+launch.  Every call here fails validation, so nothing reaches a device (the
+fake pointers are never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_masked_amd import bmattn as bm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # a non-NULL, 16-byte aligned value that is never dereferenced
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "bmattn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bmattn_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _header_functions()
+    assert len(names) >= 10
+    L = bm.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(bm.EXPORTS)
+
+
+def test_version_and_status_strings():
+    L = bm.lib()
+    assert L.bmattn_abi_version() == 1
+    assert L.bmattn_status_string(0) == b"ok"
+    assert L.bmattn_status_string(2) == b"unsupported configuration"
+    assert L.bmattn_status_string(99) == b"unknown status"
+
+
+def _desc(kind=bm.MASK_CAUSAL, n=2, mq=100, mk=100, tq=150, tk=150, ids=True):
+    d = bm.MaskDescC(kind, n, mq, mk, tq, tk, 1, 0, FAKE, FAKE,
+                     FAKE if ids else None, FAKE if ids else None, FAKE if ids else None,
+                     FAKE if ids else None, FAKE if ids else None)
+    return d
+
+
+def _call_shape(d, bm_, bn_):
+    n_qt, n_kt = ctypes.c_int32(), ctypes.c_int32()
+    rows, tiles = ctypes.c_int64(), ctypes.c_int64()
+    rc = bm.lib().bmattn_block_mask_shape(ctypes.byref(d), bm_, bn_, ctypes.byref(n_qt),
+                                          ctypes.byref(n_kt), ctypes.byref(rows), ctypes.byref(tiles))
+    return rc, n_qt.value, n_kt.value, rows.value, tiles.value
+
+
+def test_block_mask_shape_host_only():
+    rc, n_qt, n_kt, rows, tiles = _call_shape(_desc(), 128, 64)
+    assert rc == 0 and (n_qt, n_kt, rows, tiles) == (1, 2, 2, 4)
+    rc, n_qt, n_kt, rows, tiles = _call_shape(_desc(mq=257, mk=20480), 128, 64)
+    assert rc == 0 and (n_qt, n_kt) == (3, 320) and rows == 6 and tiles == 6 * 320
+
+
+@pytest.mark.parametrize("bad", [
+    dict(kind=7), dict(n=0), dict(mq=0), dict(mk=0), dict(tq=-1),
+])
+def test_desc_rejected(bad):
+    rc, *_ = _call_shape(_desc(**bad), 128, 64)
+    assert rc == 1
+    assert bm.lib().bmattn_last_error()
+
+
+@pytest.mark.parametrize("kind", [bm.MASK_SHARED_PREFIX, bm.MASK_STRIP_THINKING])
+def test_missing_ids_rejected(kind):
+    rc, *_ = _call_shape(_desc(kind=kind, ids=False), 128, 64)
+    assert rc == 1
+    assert b"needs" in bm.lib().bmattn_last_error()
+
+
+@pytest.mark.parametrize("bmn", [(0, 64), (128, 0), (2048, 64), (128, 1025)])
+def test_tile_shape_out_of_range(bmn):
+    rc, *_ = _call_shape(_desc(), *bmn)
+    assert rc == 2
+
+
+def _tiles(d, block_m=128, block_n=64, **over):
+    rc, n_qt, n_kt, rows, tiles = _call_shape(d, block_m, block_n)
+    assert rc == 0
+    t = bm.BlockMaskC(block_m, block_n, d.n_seqs, n_qt, n_kt, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    for k, v in over.items():
+        setattr(t, k, v)
+    return t
+
+
+def test_build_rejects_shape_mismatch_and_nulls():
+    L = bm.lib()
+    d = _desc()
+    t = _tiles(d, n_kt=99)
+    assert L.bmattn_build_block_mask(ctypes.byref(d), ctypes.byref(t), None) == 1
+    t = _tiles(d, full_idx=None)
+    assert L.bmattn_build_block_mask(ctypes.byref(d), ctypes.byref(t), None) == 1
+    assert L.bmattn_build_block_mask(None, ctypes.byref(_tiles(d)), None) == 1
+
+
+def _args(**over):
+    a = bm.FwdArgsC(bm.BF16, 4, 128, 16, FAKE, 512, 128, FAKE, 512, 128, FAKE, 512, 128,
+                    FAKE, 512, 128, None, 0, None, 0, 0, 0.0, 0, None, 0)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(head_dim=96), 2),
+    (dict(dtype=5), 2),
+    (dict(num_heads=0), 1),
+    (dict(q=None), 1),
+    (dict(k=FAKE + 8), 3),
+    (dict(q_stride_tok=513), 3),
+    (dict(scale=float("nan")), 1),
+    (dict(lse=FAKE, lse_stride_head=3), 1),
+    (dict(block_table=FAKE, page_size=0, num_pages=10, block_table_stride=100), 1),
+    (dict(block_table=FAKE, page_size=16, num_pages=10, block_table_stride=2), 1),
+])
+def test_forward_rejected_before_launch(over, code):
+    L = bm.lib()
+    d = _desc()
+    t = _tiles(d)
+    a = _args(**over)
+    assert L.bmattn_forward(ctypes.byref(a), ctypes.byref(d), ctypes.byref(t), None) == code
+    assert L.bmattn_last_error()
+
+
+def test_forward_rejects_uncompiled_tile_shape():
+    L = bm.lib()
+    d = _desc()
+    t = _tiles(d, block_m=64, block_n=64)
+    assert L.bmattn_forward(ctypes.byref(_args()), ctypes.byref(d), ctypes.byref(t), None) == 2
+    assert b"tile shape" in L.bmattn_last_error()
+
+
+def test_decode_requires_workspace():
+    L = bm.lib()
+    d = _desc(mq=1, tq=2)
+    t = _tiles(d, block_m=1, block_n=64)
+    a = _args()
+    n = ctypes.c_size_t()
+    assert L.bmattn_forward_workspace_size(ctypes.byref(a), ctypes.byref(d), ctypes.byref(t),
+                                           ctypes.byref(n)) == 0
+    # rows 2 x splits ceil(2/8)=1 x H 4 x (D 128 + 2) floats
+    assert n.value == 2 * 1 * 4 * 130 * 4
+    assert L.bmattn_forward(ctypes.byref(a), ctypes.byref(d), ctypes.byref(t), None) == 5
+    a = _args(workspace=FAKE, workspace_bytes=n.value - 4)
+    assert L.bmattn_forward(ctypes.byref(a), ctypes.byref(d), ctypes.byref(t), None) == 5
+
+
+def test_prefill_needs_no_workspace():
+    L = bm.lib()
+    d = _desc()
+    t = _tiles(d)
+    n = ctypes.c_size_t(123)
+    assert L.bmattn_forward_workspace_size(ctypes.byref(_args()), ctypes.byref(d), ctypes.byref(t),
+                                           ctypes.byref(n)) == 0
+    assert n.value == 0
+
+
+def test_gather_and_debug_and_validate_rejections():
+    L = bm.lib()
+    d = _desc()
+    assert L.bmattn_paged_gather(FAKE, 512, 128, 3, 4, 128, 16, 10, FAKE, 100, ctypes.byref(d),
+                                 FAKE, None) == 1
+    assert L.bmattn_paged_gather(FAKE, 512, 128, 2, 4, 128, 16, 10, FAKE, 2, ctypes.byref(d),
+                                 FAKE, None) == 1
+    assert L.bmattn_paged_gather(FAKE, 513, 128, 2, 4, 128, 16, 10, FAKE, 100, ctypes.byref(d),
+                                 FAKE, None) == 3
+    t = _tiles(d)
+    assert L.bmattn_debug_dense_mask(ctypes.byref(d), ctypes.byref(t), 5, FAKE, 1 << 20, None) == 1
+    assert L.bmattn_debug_dense_mask(ctypes.byref(d), ctypes.byref(t), 0, FAKE, 3, None) == 1
+    assert L.bmattn_validate(ctypes.byref(d), None, 0, 0, 0, None, None) == 1
+    assert L.bmattn_validate(ctypes.byref(d), FAKE, 0, 16, 10, FAKE, None) == 1

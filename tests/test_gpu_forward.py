@@ -1,0 +1,296 @@
+"""GPU forward vs the float64 oracle (O and LSE within tolerance), on small
+layouts that span several tiles with ragged tails, on every named workload
+at full size (sampled rows where the oracle would be slow), and the
+invariants of the forward: run-to-run bit-reproducibility, packing
+invariance, paged == contiguous, and untouched unreachable K/V."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from block_sparse_masked_amd import bmattn as bm
+from oracle import forward as oforward
+
+import _hip
+from _hip import DEV, say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_causal_f32_config():
+    lay = synth.config("causal_f32")
+    say("forward causal_f32 (1x2x256x64)")
+    o, lse, q, k, v, desc, t = _hip.run_dense(lay, seed=0)
+    O, L = _hip.oracle_dense(lay, q, k, v)
+    _hip.check_close(o, lse, O, L, "f32", "causal_f32")
+
+
+def test_page_example_noncausal_and_causal():
+    # Triton from First Principles, Ch. 21, section 21.2's script inputs: the
+    # library's FULL and CAUSAL forwards differ by the printed 1.7221667...
+    torch.manual_seed(0)
+    q, k, v = torch.randn(20, 8), torch.randn(20, 8), torch.randn(20, 8)
+    pad = lambda x: torch.nn.functional.pad(x, (0, 56)).reshape(20, 1, 64)
+    outs = {}
+    for kind in ("full", "causal"):
+        lay = synth.Layout("page", kind, "f32", 1, 64, [20], [20])
+        desc = _hip.desc_for(lay)
+        t = bm.build_block_mask(desc, 128, 64)
+        # zero-padded head_dim 64 keeps q.k; the scale stays 1/sqrt(8)
+        o, _ = bm.forward(pad(q).to(DEV), pad(k).to(DEV), pad(v).to(DEV), desc, t,
+                          scale=1 / math.sqrt(8))
+        outs[kind] = o.cpu()[:, 0, :8]
+    diff = (outs["full"] - outs["causal"]).abs().max().item()
+    assert abs(diff - 1.7221667766571045) < 1e-5
+
+
+CASES = []
+for kind in synth.KINDS:
+    for dtype, D in (("f32", 64), ("bf16", 128), ("bf16", 64), ("f32", 128)):
+        CASES.append((kind, dtype, D))
+
+
+@pytest.mark.parametrize("kind,dtype,D", CASES)
+def test_prefill_random_layouts(kind, dtype, D):
+    rng = np.random.default_rng(7 + len(kind) + D)
+    for trial in range(2):
+        lay = synth.random_layout(rng, kind, n_seqs=3, max_len=330, min_len=1, H=2, D=D,
+                                  dtype=dtype)
+        say(f"prefill kind={kind} dtype={dtype} D={D} lens={lay.seqlens_q}")
+        o, lse, q, k, v, desc, t = _hip.run_dense(lay, seed=trial)
+        O, L = _hip.oracle_dense(lay, q, k, v)
+        _hip.check_close(o, lse, O, L, dtype, f"{kind}/{dtype}/D{D}")
+
+
+@pytest.mark.parametrize("kind", synth.KINDS)
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_prefill_paged(kind, dtype, D):
+    rng = np.random.default_rng(31 + D)
+    lay = synth.random_layout(rng, kind, n_seqs=3, max_len=300, min_len=60, H=2, D=D, dtype=dtype,
+                              paged=True, page_size=16)
+    q, kp, vp, bt = synth.make_paged_kv(lay, seed=4, device="cpu", extra_pages=3)
+    desc = _hip.desc_for(lay)
+    t = bm.build_block_mask(desc, 128, 64)
+    say(f"prefill paged kind={kind} dtype={dtype} lens={lay.seqlens_q}")
+    o, lse = bm.forward(q.to(DEV), kp.to(DEV), vp.to(DEV), desc, t, block_table=bt.to(DEV))
+    O, L = oforward.forward(lay, q, k_pool=kp, v_pool=vp, block_table=bt)
+    _hip.check_close(o, lse, O, L, dtype, f"paged {kind}")
+
+
+@pytest.mark.parametrize("kind", synth.KINDS)
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64), ("bf16", 64)])
+def test_decode_layouts(kind, paged, dtype, D):
+    rng = np.random.default_rng(53 + D + paged)
+    for nq in (1, 3):
+        lay = synth.random_layout(rng, kind, n_seqs=4, max_len=900, min_len=1, H=5, D=D,
+                                  dtype=dtype, decode_q=nq, paged=paged, page_size=16)
+        desc = _hip.desc_for(lay)
+        t = bm.build_block_mask(desc, 1, 64)
+        say(f"decode kind={kind} paged={paged} dtype={dtype} D={D} q={nq} ctx={lay.seqlens_k}")
+        if paged:
+            q, kp, vp, bt = synth.make_paged_kv(lay, seed=nq, device="cpu", extra_pages=2)
+            o, lse = bm.forward(q.to(DEV), kp.to(DEV), vp.to(DEV), desc, t, block_table=bt.to(DEV))
+            O, L = oforward.forward(lay, q, k_pool=kp, v_pool=vp, block_table=bt)
+        else:
+            q, k, v = synth.make_dense_qkv(lay, seed=nq, device="cpu")
+            o, lse = bm.forward(q.to(DEV), k.to(DEV), v.to(DEV), desc, t)
+            O, L = oforward.forward(lay, q, k, v)
+        _hip.check_close(o, lse, O, L, dtype, f"decode {kind}")
+
+
+def test_empty_sequences_and_rows_without_keys():
+    # Sequences of length 0 write nothing; with more queries than keys the
+    # first rows see no key: O = 0 and LSE = -inf.
+    lay = synth.Layout("edge", "causal", "f32", 1, 64, [0, 5, 3], [0, 5, 1])
+    q, k, v = synth.make_dense_qkv(lay, seed=0)
+    desc = _hip.desc_for(lay)
+    for BM in (128, 1):
+        t = bm.build_block_mask(desc, BM, 64)
+        say(f"edge rows BM={BM}")
+        o, lse = bm.forward(q.to(DEV), k.to(DEV), v.to(DEV), desc, t)
+        O, L = oforward.forward(lay, q, k, v)
+        _hip.check_close(o, lse, O, L, "f32", "edge")
+        assert np.isneginf(lse.cpu().numpy()[0, 5:7]).all()
+
+
+def test_packed_documents_full_size():
+    lay = synth.config("packed_documents")
+    say(f"forward packed_documents lens={lay.seqlens_q}")
+    o, lse, q, k, v, desc, t = _hip.run_dense(lay, seed=0)
+    O, L = _hip.oracle_dense(lay, q, k, v)
+    mx, mean = _hip.check_close(o, lse, O, L, "bf16", "packed_documents")
+    say(f"packed_documents max-abs {mx:.3e} mean-abs {mean:.3e}")
+
+
+def _sample_rows(T, rng, extra=()):
+    rows = set(rng.choice(T, size=min(T, 48), replace=False).tolist())
+    rows.update([0, 1, T - 1, T - 2] + [r for r in extra if 0 <= r < T])
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["shared_prefix", "strip_thinking"])
+def test_single_sequence_workloads_sampled(name):
+    lay = synth.config(name)
+    say(f"forward {name} full size")
+    o, lse, q, k, v, desc, t = _hip.run_dense(lay, seed=0)
+    rng = np.random.default_rng(5)
+    T = lay.total_q
+    boundaries = [4095, 4096, 4097, 5119, 5120] if name == "shared_prefix" else [255, 256, 1791, 1792, 2303, 2304]
+    rows = _sample_rows(T, rng, boundaries)
+    on, ln = o.float().cpu().numpy(), lse.cpu().numpy()
+    worst = 0.0
+    for h in (0, 13, lay.num_heads - 1):
+        qh, kh, vh = (oforward.head_slice(x, h) for x in (q, k, v))
+        O, L = oforward.sequence_head(lay, 0, qh, kh, vh, rows=rows)
+        err = np.abs(on[rows, h] - O)
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3, (h, err.max(), err.mean())
+        assert np.abs(ln[h, rows] - L).max() <= 2e-2
+        worst = max(worst, float(err.max()))
+    say(f"{name} sampled max-abs {worst:.3e}")
+
+
+def test_paged_decode_full_size_sampled():
+    lay = synth.config("paged_decode")
+    say(f"forward paged_decode full size, {lay.total_k} context tokens")
+    q, kp, vp, bt = synth.make_paged_kv(lay, seed=0, device=DEV)
+    desc = _hip.desc_for(lay)
+    t = bm.build_block_mask(desc, 1, 64)
+    o, lse = bm.forward(q, kp, vp, desc, t, block_table=bt)
+    torch.cuda.synchronize()
+    ctx = np.array(lay.seqlens_k)
+    seqs = sorted({int(ctx.argmax()), int(ctx.argmin()), 7, 40})
+    on, ln = o.float().cpu().numpy(), lse.cpu().numpy()
+    for s in seqs:
+        n = -(-ctx[s] // 16)
+        pages = bt[s, :n].long()
+        sub = synth.Layout("one", "causal", "bf16", lay.num_heads, lay.head_dim, [1], [int(ctx[s])],
+                           paged=True, page_size=16)
+        bt_sub = np.arange(n, dtype=np.int32)[None, :]
+        for h in (0, 31):
+            kh = oforward.to_f64(kp[pages, :, h])
+            vh = oforward.to_f64(vp[pages, :, h])
+            qh = oforward.to_f64(q[s:s + 1, h])
+            O, L = oforward.sequence_head(sub, 0, qh, kh, vh, block_table=bt_sub)
+            err = np.abs(on[s, h] - O[0])
+            assert err.max() <= 2e-2, (s, h, err.max())
+            assert abs(ln[h, s] - L[0]) <= 2e-2
+    say("paged_decode sampled rows ok")
+
+
+def test_bit_reproducible_run_to_run():
+    lay = synth.shared_prefix(prefix=1024, n_suffix=4, suffix=512, H=4)
+    q, k, v = (x.to(DEV) for x in synth.make_dense_qkv(lay, seed=3, device="cpu"))
+    desc = _hip.desc_for(lay)
+    t = bm.build_block_mask(desc, 128, 64)
+    say("reproducibility x3")
+    o1, l1 = bm.forward(q, k, v, desc, t)
+    o2, l2 = bm.forward(q, k, v, desc, t)
+    t2 = bm.build_block_mask(desc, 128, 64)
+    o3, l3 = bm.forward(q, k, v, desc, t2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+@pytest.mark.parametrize("BM", [128, 1])
+def test_packing_invariance_bit_exact(BM):
+    # Each packed document's output is bit-identical to the document run alone.
+    lay = synth.packed_documents(seed=2, n_docs=4, lo=30, hi=700, H=4)
+    if BM == 1:
+        lay = synth.Layout("decode", "causal", "bf16", 4, 128, [1] * 4, lay.seqlens_k)
+    q, k, v = synth.make_dense_qkv(lay, seed=2, device="cpu")
+    desc = _hip.desc_for(lay)
+    t = bm.build_block_mask(desc, BM, 64)
+    say(f"packing invariance BM={BM} lens={lay.seqlens_k}")
+    o, l = bm.forward(q.to(DEV), k.to(DEV), v.to(DEV), desc, t)
+    cq, ck = lay.cu_q, lay.cu_k
+    for s in range(lay.n_seqs):
+        one = synth.Layout("one", "causal", "bf16", 4, 128, [lay.seqlens_q[s]], [lay.seqlens_k[s]])
+        d1 = _hip.desc_for(one)
+        t1 = bm.build_block_mask(d1, BM, 64)
+        o1, l1 = bm.forward(q[cq[s]:cq[s + 1]].to(DEV), k[ck[s]:ck[s + 1]].to(DEV),
+                            v[ck[s]:ck[s + 1]].to(DEV), d1, t1)
+        assert torch.equal(o[cq[s]:cq[s + 1]], o1), s
+        assert torch.equal(l[:, cq[s]:cq[s + 1]], l1), s
+
+
+@pytest.mark.parametrize("kind", ["causal", "strip_thinking"])
+def test_paged_equals_contiguous_bit_exact(kind):
+    rng = np.random.default_rng(77)
+    lay = synth.random_layout(rng, kind, n_seqs=3, max_len=400, min_len=100, H=2, D=128,
+                              dtype="bf16", paged=True, page_size=16)
+    q, kp, vp, bt = synth.make_paged_kv(lay, seed=9, device="cpu", extra_pages=4)
+    desc = _hip.desc_for(lay)
+    t = bm.build_block_mask(desc, 128, 64)
+    say(f"paged == contiguous kind={kind}")
+    op, lp = bm.forward(q.to(DEV), kp.to(DEV), vp.to(DEV), desc, t, block_table=bt.to(DEV))
+    kc = bm.paged_gather(kp.to(DEV), bt.to(DEV), desc)
+    vc = bm.paged_gather(vp.to(DEV), bt.to(DEV), desc)
+    oc, lc = bm.forward(q.to(DEV), kc, vc, desc, t)
+    torch.cuda.synchronize()
+    assert torch.equal(op, oc) and torch.equal(lp, lc)
+
+
+@pytest.mark.parametrize("BM", [128, 1])
+def test_unreachable_kv_never_read(BM):
+    # NaN in pool pages no sequence uses, in page slots past each context and
+    # in rows past the packed K/V: the outputs are bit-identical to a clean run.
+    lay = synth.paged_decode(seed=4, n_seqs=5, lo=40, hi=700, page_size=16, H=2, D=128)
+    if BM == 128:
+        lay = synth.Layout("prefill", "causal", "bf16", 2, 128, lay.seqlens_k, lay.seqlens_k,
+                           paged=True, page_size=16)
+    q, kp, vp, bt = synth.make_paged_kv(lay, seed=4, device="cpu", extra_pages=6)
+    desc = _hip.desc_for(lay)
+    t = bm.build_block_mask(desc, BM, 64)
+    say(f"NaN poisoning BM={BM}")
+    clean = bm.forward(q.to(DEV), kp.to(DEV), vp.to(DEV), desc, t, block_table=bt.to(DEV))
+    kpn, vpn = kp.clone(), vp.clone()
+    used = set()
+    for s, c in enumerate(lay.seqlens_k):
+        n = -(-c // 16)
+        used.update(bt[s, :n].tolist())
+        last = int(bt[s, n - 1])
+        tail = c - (n - 1) * 16
+        kpn[last, tail:] = float("nan")
+        vpn[last, tail:] = float("nan")
+    for pg in range(kp.shape[0]):
+        if pg not in used:
+            kpn[pg] = float("nan")
+            vpn[pg] = float("nan")
+    dirty = bm.forward(q.to(DEV), kpn.to(DEV), vpn.to(DEV), desc, t, block_table=bt.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(clean[0], dirty[0]) and torch.equal(clean[1], dirty[1])
+    # Contiguous K/V with NaN rows past the last key.
+    kc = bm.paged_gather(kp.to(DEV), bt.to(DEV), desc)
+    vc = bm.paged_gather(vp.to(DEV), bt.to(DEV), desc)
+    T = kc.shape[0]
+    kbig = torch.full((T + 200, 2, 128), float("nan"), dtype=kc.dtype, device=DEV)
+    vbig = kbig.clone()
+    kbig[:T] = kc
+    vbig[:T] = vc
+    a = bm.forward(q.to(DEV), kc, vc, desc, t)
+    b = bm.forward(q.to(DEV), kbig[:T], vbig[:T], desc, t)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert torch.isfinite(a[0].float()).all()
+
+
+def test_strided_views_and_explicit_scale():
+    # Q/K/V as head-strided views of one fused buffer; O into a strided view.
+    lay = synth.causal_single(L=300, H=3, D=128, dtype="bf16")
+    fused = synth.make_dense_qkv(synth.causal_single(L=300, H=9, D=128, dtype="bf16"), seed=1)[0]
+    q, k, v = fused[:, 0:3], fused[:, 3:6], fused[:, 6:9]
+    desc = _hip.desc_for(lay)
+    t = bm.build_block_mask(desc, 128, 64)
+    out_buf = torch.zeros(300, 6, 128, dtype=torch.bfloat16, device=DEV)
+    say("strided views")
+    fd = fused.to(DEV)
+    o, lse = bm.forward(fd[:, 0:3], fd[:, 3:6], fd[:, 6:9], desc, t, out=out_buf[:, 1:4], scale=0.05)
+    torch.cuda.synchronize()
+    O, L = oforward.forward(lay, q, k, v, scale=0.05)
+    _hip.check_close(out_buf[:, 1:4], lse, O, L, "bf16", "strided")
+    assert torch.count_nonzero(out_buf[:, 0]) == 0 and torch.count_nonzero(out_buf[:, 4:]) == 0

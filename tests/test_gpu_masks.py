@@ -1,0 +1,119 @@
+"""GPU vs oracle, bit-exact: tile classes, kv-tile lists, the row schedule,
+the dense-mask export and the paged gather."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from block_sparse_masked_amd import bmattn as bm
+from oracle import paged as opaged
+
+import _hip
+from _hip import DEV, say
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(1, 1), (2, 3), (4, 4), (13, 8), (16, 64), (64, 16), (128, 64), (1, 64), (37, 29),
+          (128, 128), (256, 64)]
+KIND_SEED = {"full": 1, "causal": 2, "shared_prefix": 3, "strip_thinking": 4}
+
+
+@pytest.mark.parametrize("decode_q", [None, 1, 3])
+@pytest.mark.parametrize("kind", synth.KINDS)
+def test_tiles_bit_exact_random_layouts(kind, decode_q):
+    rng = np.random.default_rng(100 * KIND_SEED[kind] + (decode_q or 0))
+    for trial in range(3):
+        lay = synth.random_layout(rng, kind, n_seqs=3, max_len=90, decode_q=decode_q)
+        desc = _hip.desc_for(lay)
+        for BM, BN in SHAPES:
+            say(f"tiles kind={kind} decode_q={decode_q} trial={trial} lens={lay.seqlens_k} BM={BM} BN={BN}")
+            t = _hip.check_tiles(lay, desc, BM, BN)
+            _hip.check_dense(lay, desc, t)
+
+
+def test_tiles_empty_and_tiny_sequences():
+    lay = synth.Layout("edge", "causal", "f32", 1, 8, [0, 1, 5, 0], [0, 1, 5, 0])
+    desc = _hip.desc_for(lay)
+    for BM, BN in [(1, 1), (4, 4), (128, 64)]:
+        say(f"tiles empty sequences BM={BM} BN={BN}")
+        t = _hip.check_tiles(lay, desc, BM, BN)
+        _hip.check_dense(lay, desc, t)
+
+
+@pytest.mark.parametrize("name", ["causal_f32", "packed_documents", "shared_prefix",
+                                  "strip_thinking"])
+def test_tiles_bit_exact_named_workloads(name):
+    lay = synth.config(name)
+    desc = _hip.desc_for(lay)
+    say(f"tiles {name} at 128x64")
+    t = _hip.check_tiles(lay, desc, 128, 64)
+    say(f"dense export {name}")
+    _hip.check_dense(lay, desc, t)
+
+
+def test_tiles_bit_exact_paged_decode():
+    lay = synth.config("paged_decode")
+    desc = _hip.desc_for(lay)
+    say("tiles paged_decode at 1x64")
+    t = _hip.check_tiles(lay, desc, 1, 64)
+    # every listed tile but a sequence's ragged last one is FULL
+    fc = t.full_cnt.cpu().numpy()
+    pc = t.part_cnt.cpu().numpy()
+    ctx = np.array(lay.seqlens_k)
+    assert np.array_equal(fc, ctx // 64)
+    assert np.array_equal(pc, (ctx % 64 != 0).astype(np.int32))
+
+
+def test_validate_flags():
+    lay = synth.paged_decode(seed=1, n_seqs=4, lo=5, hi=60, page_size=4, H=1, D=8, dtype="f32")
+    desc = _hip.desc_for(lay)
+    q, kp, vp, bt = synth.make_paged_kv(lay, seed=1, device="cpu")
+    btd = bt.to(DEV)
+    say("validate: good description")
+    assert bm.validate(desc, btd, 4, kp.shape[0]) == 0
+    bad = btd.clone()
+    bad[0, 0] = kp.shape[0]
+    say("validate: bad block table entry")
+    assert bm.validate(desc, bad, 4, kp.shape[0]) == 8
+    cu = torch.tensor(lay.cu_k, dtype=torch.int32)
+    cu[2] = cu[1] - 1  # a decreasing offset
+    d2 = bm.MaskDesc.create("causal", lay.cu_q, cu, desc.max_seqlen_q, desc.max_seqlen_k, device=DEV)
+    say("validate: decreasing cu_seqlens_k")
+    assert bm.validate(d2) & 2
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("page_size", [1, 3, 4, 16])
+def test_paged_gather_byte_equal(dtype, page_size):
+    rng = np.random.default_rng(page_size)
+    for trial in range(2):
+        ctx = rng.integers(1, 200, size=4).tolist() + [13]
+        lay = synth.Layout("gather", "causal", dtype, 3, 64 if dtype == "f32" else 128,
+                           [1] * len(ctx), ctx, paged=True, page_size=page_size)
+        q, kp, vp, bt = synth.make_paged_kv(lay, seed=trial, device="cpu", extra_pages=5,
+                                            table_pad=2)
+        desc = _hip.desc_for(lay)
+        say(f"gather dtype={dtype} page={page_size} ctx={ctx}")
+        got = bm.paged_gather(kp.to(DEV), bt.to(DEV), desc).cpu()
+        raw = kp.view(torch.int16) if dtype == "bf16" else kp.view(torch.int32)
+        gotr = got.view(torch.int16) if dtype == "bf16" else got.view(torch.int32)
+        cu = lay.cu_k
+        for s in range(lay.n_seqs):
+            for tile in (1, 13, None):
+                want = opaged.paged_gather(raw.numpy(), bt[s].numpy(), ctx[s], page_size, tile=tile)
+                assert want.tobytes() == gotr[cu[s]:cu[s + 1]].numpy().tobytes(), (s, tile)
+
+
+def test_paged_gather_byte_equal_decode_contexts():
+    # The paged-decode workload's contexts and page table at 2 heads.
+    lay = synth.paged_decode(seed=0, H=2)
+    q, kp, vp, bt = synth.make_paged_kv(lay, seed=0, device="cpu")
+    desc = _hip.desc_for(lay)
+    say(f"gather paged_decode contexts, total {lay.total_k} tokens")
+    got = bm.paged_gather(kp.to(DEV), bt.to(DEV), desc).cpu().view(torch.int16).numpy()
+    raw = kp.view(torch.int16).numpy()
+    cu = lay.cu_k
+    for s in range(lay.n_seqs):
+        want = opaged.paged_gather(raw, bt[s].numpy(), lay.seqlens_k[s], 16)
+        assert want.tobytes() == got[cu[s]:cu[s + 1]].tobytes(), s
