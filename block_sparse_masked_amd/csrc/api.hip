@@ -272,6 +272,7 @@ int bmattn_forward(const bmattn_fwd_args* a, const bmattn_mask_desc* desc,
   p.bt_stride = a->block_table_stride;
   p.num_pages = a->num_pages;
   p.page_size = a->page_size;
+  p.page_shift = page_shift_of(a->page_size);
   const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->head_dim);
   p.scale_log2 = scale * 1.4426950408889634f;
   const bool paged = a->block_table != nullptr;

@@ -68,31 +68,68 @@ __device__ __forceinline__ QIds load_qids(const MaskDev& m, const SeqBounds& b, 
   return r;
 }
 
+// Key-side ids of one key: the segment (shared-prefix) or the role and turn
+// (strip-thinking); unused fields are 0.
+struct KIds {
+  int32_t a, b;
+};
+
+__device__ __forceinline__ KIds load_kids(const MaskDev& m, const SeqBounds& b, int j) {
+  KIds r{0, 0};
+  if (j < b.lk) {
+    if (m.kind == BMATTN_MASK_SHARED_PREFIX) r.a = m.seg_k[b.k0 + j];
+    if (m.kind == BMATTN_MASK_STRIP_THINKING) {
+      r.a = m.role_k[b.k0 + j];
+      r.b = m.turn_k[b.k0 + j];
+    }
+  }
+  return r;
+}
+
 // Element predicate: is key j of the sequence visible to its query row i?
 // Query row i sits at position lk - lq + i; the causal condition keeps the
 // diagonal (j <= position).  Pairs outside the sequence are not visible.
-__device__ __forceinline__ bool visible(const MaskDev& m, const SeqBounds& b, int i, QIds qi,
-                                        int j) {
+// kid holds key j's ids (load_kids).
+__device__ __forceinline__ bool visible_ids(const MaskDev& m, const SeqBounds& b, int i, QIds qi,
+                                            int j, KIds kid) {
   if (i >= b.lq || j >= b.lk) return false;
   if (m.kind == BMATTN_MASK_FULL) return true;
   if (j > b.lk - b.lq + i) return false;
-  if (m.kind == BMATTN_MASK_SHARED_PREFIX) {
-    int32_t sk = m.seg_k[b.k0 + j];
-    return sk == 0 || sk == qi.seg;
-  }
-  if (m.kind == BMATTN_MASK_STRIP_THINKING) {
-    return !(m.role_k[b.k0 + j] == m.think_role && m.turn_k[b.k0 + j] < qi.turn);
-  }
+  if (m.kind == BMATTN_MASK_SHARED_PREFIX) return kid.a == 0 || kid.a == qi.seg;
+  if (m.kind == BMATTN_MASK_STRIP_THINKING) return !(kid.a == m.think_role && kid.b < qi.turn);
   return true;  // CAUSAL
 }
 
-// Physical pool row of logical key j of sequence s in a paged K/V.  Entries
-// outside [0, num_pages) are clamped (bmattn_validate reports them).
+__device__ __forceinline__ bool visible(const MaskDev& m, const SeqBounds& b, int i, QIds qi,
+                                        int j) {
+  return visible_ids(m, b, i, qi, j, load_kids(m, b, j));
+}
+
+// Physical pool row of logical key j of sequence s in a paged K/V: page
+// block_table[s][j / page_size], slot j % page_size.  Entries outside
+// [0, num_pages) are clamped (bmattn_validate reports them).  page_shift is
+// log2(page_size) when the page size is a power of two, else -1.
+__device__ __forceinline__ int32_t page_of(int j, int32_t page_size, int32_t page_shift) {
+  return page_shift >= 0 ? (j >> page_shift) : (j / page_size);
+}
+
+__device__ __forceinline__ int32_t page_entry(const int32_t* block_table, int64_t bt_stride, int s,
+                                              int j, int32_t page_size, int32_t page_shift) {
+  return block_table[(int64_t)s * bt_stride + page_of(j, page_size, page_shift)];
+}
+
+__device__ __forceinline__ int64_t row_in_page(int32_t entry, int j, int32_t page_size,
+                                               int32_t page_shift, int64_t num_pages) {
+  const int64_t pg = clamp64(entry, 0, num_pages - 1);
+  const int32_t slot = page_shift >= 0 ? (j & (page_size - 1)) : (j % page_size);
+  return pg * page_size + slot;
+}
+
 __device__ __forceinline__ int64_t paged_row(const int32_t* block_table, int64_t bt_stride, int s,
-                                             int j, int32_t page_size, int64_t num_pages) {
-  int32_t pg = block_table[(int64_t)s * bt_stride + j / page_size];
-  int64_t p = clamp64(pg, 0, num_pages - 1);
-  return p * page_size + (j % page_size);
+                                             int j, int32_t page_size, int32_t page_shift,
+                                             int64_t num_pages) {
+  return row_in_page(page_entry(block_table, bt_stride, s, j, page_size, page_shift), j, page_size,
+                     page_shift, num_pages);
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs of the chip.  This

@@ -104,11 +104,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(FwdDev p) {
   }
   const char* kbase = static_cast<const char*>(p.k);
   const char* vbase = static_cast<const char*>(p.v);
-  auto addr = [&](const char* base, int64_t st, int64_t sh, int j) -> const char* {
-    const int64_t r = PAGED ? paged_row(p.block_table, p.bt_stride, s, j, p.page_size, p.num_pages)
-                            : sb.k0 + j;
-    return base + (r * st + (int64_t)h * sh) * kElem + c * 16;
-  };
+  const int64_t k_off = (int64_t)h * p.k_sh * kElem + c * 16;
+  const int64_t v_off = (int64_t)h * p.v_sh * kElem + c * 16;
+  const int64_t k_rs = p.k_st * kElem, v_rs = p.v_st * kElem;
 
   float acc[kEpc];
 #pragma unroll
@@ -123,19 +121,41 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(FwdDev p) {
     const bool masked = e >= nfull;
     const int kt = masked ? plist[e - nfull] : flist[e];
     for (int sb0 = 0; sb0 < kSteps; sb0 += kSub) {
+      // All row lookups first (one wait for the block-table reads), then
+      // every K and V load of the sub-block in flight together.
+      int64_t rows[kSub];
+      if constexpr (PAGED) {
+        int32_t pe[kSub];
+#pragma unroll
+        for (int st = 0; st < kSub; ++st) {
+          const int j = min(kt * kBN + (sb0 + st) * kTpi + tg, sb.lk - 1);
+          pe[st] = page_entry(p.block_table, p.bt_stride, s, j, p.page_size, p.page_shift);
+        }
+#pragma unroll
+        for (int st = 0; st < kSub; ++st) {
+          const int j = kt * kBN + (sb0 + st) * kTpi + tg;
+          rows[st] = (!masked || j < sb.lk)
+                         ? row_in_page(pe[st], j, p.page_size, p.page_shift, p.num_pages)
+                         : -1;
+        }
+      } else {
+#pragma unroll
+        for (int st = 0; st < kSub; ++st) {
+          const int j = kt * kBN + (sb0 + st) * kTpi + tg;
+          rows[st] = (!masked || j < sb.lk) ? sb.k0 + j : -1;
+        }
+      }
       uint4 kr[kSub];
       uint4 vr[kSub];
 #pragma unroll
       for (int st = 0; st < kSub; ++st) {
-        const int j = kt * kBN + (sb0 + st) * kTpi + tg;
-        kr[st] = (!masked || j < sb.lk) ? *reinterpret_cast<const uint4*>(addr(kbase, p.k_st, p.k_sh, j))
-                                        : make_uint4(0, 0, 0, 0);
+        kr[st] = rows[st] >= 0 ? *reinterpret_cast<const uint4*>(kbase + rows[st] * k_rs + k_off)
+                               : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int st = 0; st < kSub; ++st) {
-        const int j = kt * kBN + (sb0 + st) * kTpi + tg;
-        vr[st] = (!masked || j < sb.lk) ? *reinterpret_cast<const uint4*>(addr(vbase, p.v_st, p.v_sh, j))
-                                        : make_uint4(0, 0, 0, 0);
+        vr[st] = rows[st] >= 0 ? *reinterpret_cast<const uint4*>(vbase + rows[st] * v_rs + v_off)
+                               : make_uint4(0, 0, 0, 0);
       }
       float sc[kSub];
 #pragma unroll

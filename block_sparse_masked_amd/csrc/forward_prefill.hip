@@ -50,7 +50,8 @@ struct Cfg {
   static constexpr int kVP = kBN * kElem + 16;       // V^T row pitch in LDS (bytes)
   static constexpr int kKBuf = kBN * kKP;
   static constexpr int kVBuf = D * kVP;
-  static constexpr int kStage = kKBuf + kVBuf;
+  static constexpr int kIdBuf = 2 * kBN * 4;              // key ids of a PARTIAL tile
+  static constexpr int kStage = kKBuf + kVBuf + kIdBuf;
   static constexpr int kKChunks = kBN * kCh / kThreads;  // K chunks per thread
   static constexpr int kKpt = kBN * kCh / kThreads;      // keys per thread (V staging)
   static constexpr int kDT = D / 32;                     // 32-wide output d tiles
@@ -81,50 +82,75 @@ template <typename T, int D, bool PAGED>
 struct Prefill {
   using C = Cfg<T, D>;
 
-  // Global address (bytes) of key row j of sequence s for head h.
-  static __device__ __forceinline__ const char* krow(const FwdDev& p, const char* base,
-                                                      int64_t st_tok, int64_t st_head,
-                                                      const SeqBounds& sb, int s, int h, int j) {
-    int64_t r = PAGED ? paged_row(p.block_table, p.bt_stride, s, j, p.page_size, p.num_pages)
-                      : sb.k0 + j;
-    return base + (r * st_tok + (int64_t)h * st_head) * C::kElem;
-  }
-
   // Global -> registers for one kv tile.  Rows past the sequence (only in
   // PARTIAL tiles) are zero and never read.
   static __device__ __forceinline__ void load_tile(const FwdDev& p, const SeqBounds& sb, int s,
                                                    int h, int kt, bool masked, int tid,
                                                    uint4 (&kr)[C::kKChunks],
-                                                   uint4 (&vr)[C::kKpt]) {
-    const char* kb = static_cast<const char*>(p.k);
-    const char* vb = static_cast<const char*>(p.v);
+                                                   uint4 (&vr)[C::kKpt], KIds& kid) {
+    if (masked && tid < kBN) kid = load_kids(p.mask, sb, kt * kBN + tid);
+    const char* kb = static_cast<const char*>(p.k) + (int64_t)h * p.k_sh * C::kElem;
+    const char* vb = static_cast<const char*>(p.v) + (int64_t)h * p.v_sh * C::kElem;
+    // Physical rows first (block-table reads all in flight together), then
+    // the tile loads.  Rows past the sequence are marked -1.
+    int64_t krows[C::kKChunks], vrows[C::kKpt];
+    const int ch = tid % C::kCh, kg = tid / C::kCh;
+    if constexpr (PAGED) {
+      int32_t kpe[C::kKChunks], vpe[C::kKpt];
 #pragma unroll
-    for (int u = 0; u < C::kKChunks; ++u) {
-      const int c = tid + kThreads * u;
-      const int row = c / C::kCh, ch = c % C::kCh;
-      const int j = kt * kBN + row;
-      if (!masked || j < sb.lk) {
-        kr[u] = *reinterpret_cast<const uint4*>(krow(p, kb, p.k_st, p.k_sh, sb, s, h, j) + ch * 16);
-      } else {
-        kr[u] = make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < C::kKChunks; ++u) {
+        const int j = min(kt * kBN + (tid + kThreads * u) / C::kCh, sb.lk - 1);
+        kpe[u] = page_entry(p.block_table, p.bt_stride, s, j, p.page_size, p.page_shift);
+      }
+#pragma unroll
+      for (int u = 0; u < C::kKpt; ++u) {
+        const int j = min(kt * kBN + kg * C::kKpt + u, sb.lk - 1);
+        vpe[u] = page_entry(p.block_table, p.bt_stride, s, j, p.page_size, p.page_shift);
+      }
+#pragma unroll
+      for (int u = 0; u < C::kKChunks; ++u) {
+        const int j = kt * kBN + (tid + kThreads * u) / C::kCh;
+        krows[u] = (!masked || j < sb.lk) ? row_in_page(kpe[u], j, p.page_size, p.page_shift, p.num_pages) : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < C::kKpt; ++u) {
+        const int j = kt * kBN + kg * C::kKpt + u;
+        vrows[u] = (!masked || j < sb.lk) ? row_in_page(vpe[u], j, p.page_size, p.page_shift, p.num_pages) : -1;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < C::kKChunks; ++u) {
+        const int j = kt * kBN + (tid + kThreads * u) / C::kCh;
+        krows[u] = (!masked || j < sb.lk) ? sb.k0 + j : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < C::kKpt; ++u) {
+        const int j = kt * kBN + kg * C::kKpt + u;
+        vrows[u] = (!masked || j < sb.lk) ? sb.k0 + j : -1;
       }
     }
-    const int ch = tid % C::kCh, kg = tid / C::kCh;
+#pragma unroll
+    for (int u = 0; u < C::kKChunks; ++u) {
+      const int kch = (tid + kThreads * u) % C::kCh;
+      kr[u] = krows[u] >= 0 ? *reinterpret_cast<const uint4*>(kb + krows[u] * p.k_st * C::kElem + kch * 16)
+                            : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
     for (int u = 0; u < C::kKpt; ++u) {
-      const int j = kt * kBN + kg * C::kKpt + u;
-      if (!masked || j < sb.lk) {
-        vr[u] = *reinterpret_cast<const uint4*>(krow(p, vb, p.v_st, p.v_sh, sb, s, h, j) + ch * 16);
-      } else {
-        vr[u] = make_uint4(0, 0, 0, 0);
-      }
+      vr[u] = vrows[u] >= 0 ? *reinterpret_cast<const uint4*>(vb + vrows[u] * p.v_st * C::kElem + ch * 16)
+                            : make_uint4(0, 0, 0, 0);
     }
   }
 
   // Registers -> LDS: K row-major, V transposed (V^T[d][key]).
-  static __device__ __forceinline__ void store_tile(char* stage, int tid,
+  static __device__ __forceinline__ void store_tile(char* stage, int tid, bool masked,
                                                     const uint4 (&kr)[C::kKChunks],
-                                                    const uint4 (&vr)[C::kKpt]) {
+                                                    const uint4 (&vr)[C::kKpt], const KIds& kid) {
+    if (masked && tid < kBN) {
+      int32_t* ids = reinterpret_cast<int32_t*>(stage + C::kKBuf + C::kVBuf);
+      ids[tid] = kid.a;
+      ids[kBN + tid] = kid.b;
+    }
 #pragma unroll
     for (int u = 0; u < C::kKChunks; ++u) {
       const int c = tid + kThreads * u;
@@ -183,6 +209,130 @@ struct QFrag<float, D> {
   float v[D / 2];
 };
 
+// Per-wave running state of the online softmax for its 32 query rows.
+template <int D>
+struct RowState {
+  f32x16 acc[D / 32];  // O^T accumulator: lane holds query (l % 32), 16 d rows per tile
+  float m, l;          // running max (base-2 scaled) and this lane's partial sum
+};
+
+// One kv tile: S^T = K Q^T, the element mask on PARTIAL tiles, the online
+// softmax update and acc^T += V^T P^T.
+template <typename T, int D, bool MASKED>
+__device__ __forceinline__ void tile_step(const char* Ks, const QFrag<T, D>& qf, RowState<D>& st,
+                                          const FwdDev& p, const SeqBounds& sb, int kt, int qi,
+                                          QIds qids, int g, int l32, int krow_a) {
+  using C = Cfg<T, D>;
+  const char* Vt = Ks + C::kKBuf;
+  f32x16 s0 = f32x16{}, s1 = f32x16{};
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(Ks + krow_a * C::kKP + (ks * 16 + g * 8) * 2);
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(Ks + (32 + krow_a) * C::kKP + (ks * 16 + g * 8) * 2);
+      s0 = mfma(k0, qf.v[ks], s0);
+      s1 = mfma(k1, qf.v[ks], s1);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+      const float4 k0 = *reinterpret_cast<const float4*>(Ks + krow_a * C::kKP + (g * (D / 2) + c * 4) * 4);
+      const float4 k1 = *reinterpret_cast<const float4*>(Ks + (32 + krow_a) * C::kKP + (g * (D / 2) + c * 4) * 4);
+      s0 = mfma(k0.x, qf.v[c * 4 + 0], s0);
+      s1 = mfma(k1.x, qf.v[c * 4 + 0], s1);
+      s0 = mfma(k0.y, qf.v[c * 4 + 1], s0);
+      s1 = mfma(k1.y, qf.v[c * 4 + 1], s1);
+      s0 = mfma(k0.z, qf.v[c * 4 + 2], s0);
+      s1 = mfma(k1.z, qf.v[c * 4 + 2], s1);
+      s0 = mfma(k0.w, qf.v[c * 4 + 3], s0);
+      s1 = mfma(k1.w, qf.v[c * 4 + 3], s1);
+    }
+  }
+
+  // Register r of block b holds key kt*64 + b*32 + 16*(r/8) + 8*g + r%8.
+  float x[32];
+  const float sl2 = p.scale_log2;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    x[r] = s0[r] * sl2;
+    x[16 + r] = s1[r] * sl2;
+  }
+  if constexpr (MASKED) {
+    const int32_t* ids = reinterpret_cast<const int32_t*>(Ks + C::kKBuf + C::kVBuf);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int jj = b * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
+        const KIds kid{ids[jj], ids[kBN + jj]};
+        if (!visible_ids(p.mask, sb, qi, qids, kt * kBN + jj, kid)) x[b * 16 + r] = -INFINITY;
+      }
+    }
+  }
+  float mx = x[0];
+#pragma unroll
+  for (int r = 1; r < 32; ++r) mx = fmaxf(mx, x[r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(st.m, mx);
+  const float m_use = (MASKED && m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = fast_exp2(st.m - m_use);
+  float rs = 0.f;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    x[r] = fast_exp2(x[r] - m_use);
+    rs += x[r];
+  }
+  st.l = st.l * alpha + rs;
+  st.m = m_new;
+  if (__ballot(alpha != 1.f)) {
+#pragma unroll
+    for (int dt = 0; dt < C::kDT; ++dt) st.acc[dt] *= alpha;
+  }
+
+  if constexpr (sizeof(T) == 2) {
+    bf16x8 pf[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint4 u;
+      u.x = pack_bf16x2(x[k * 8 + 0], x[k * 8 + 1]);
+      u.y = pack_bf16x2(x[k * 8 + 2], x[k * 8 + 3]);
+      u.z = pack_bf16x2(x[k * 8 + 4], x[k * 8 + 5]);
+      u.w = pack_bf16x2(x[k * 8 + 6], x[k * 8 + 7]);
+      pf[k] = __builtin_bit_cast(bf16x8, u);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+#pragma unroll
+      for (int dt = 0; dt < C::kDT; ++dt) {
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + (dt * 32 + l32) * C::kVP + (k * 16 + g * 8) * 2);
+        st.acc[dt] = mfma(vf, pf[k], st.acc[dt]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int dt = 0; dt < C::kDT; ++dt) {
+          const char* src = Vt + (dt * 32 + l32) * C::kVP + (b * 32 + 16 * hh + 8 * g) * 4;
+          const float4 v0 = *reinterpret_cast<const float4*>(src);
+          const float4 v1 = *reinterpret_cast<const float4*>(src + 16);
+          const int r0 = b * 16 + hh * 8;
+          st.acc[dt] = mfma(v0.x, x[r0 + 0], st.acc[dt]);
+          st.acc[dt] = mfma(v0.y, x[r0 + 1], st.acc[dt]);
+          st.acc[dt] = mfma(v0.z, x[r0 + 2], st.acc[dt]);
+          st.acc[dt] = mfma(v0.w, x[r0 + 3], st.acc[dt]);
+          st.acc[dt] = mfma(v1.x, x[r0 + 4], st.acc[dt]);
+          st.acc[dt] = mfma(v1.y, x[r0 + 5], st.acc[dt]);
+          st.acc[dt] = mfma(v1.z, x[r0 + 6], st.acc[dt]);
+          st.acc[dt] = mfma(v1.w, x[r0 + 7], st.acc[dt]);
+        }
+      }
+    }
+  }
+}
+
 template <typename T, int D, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(FwdDev p) {
   using C = Cfg<T, D>;
@@ -203,6 +353,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(FwdDev p) {
   const int ntiles = nfull + p.part_cnt[row];
   const int32_t* flist = p.full_idx + (int64_t)row * p.n_kt;
   const int32_t* plist = p.part_idx + (int64_t)row * p.n_kt;
+  auto tile_of = [&](int t) { return t < nfull ? flist[t] : plist[t - nfull]; };
 
   const int qi = a * kBM + wave * 32 + l32;  // query row inside the sequence
   const bool qvalid = qi < sb.lq;
@@ -233,148 +384,49 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(FwdDev p) {
     }
   }
 
-  f32x16 acc[C::kDT];
+  RowState<D> st;
 #pragma unroll
-  for (int dt = 0; dt < C::kDT; ++dt) acc[dt] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-  const float sl2 = p.scale_log2;
+  for (int dt = 0; dt < C::kDT; ++dt) st.acc[dt] = f32x16{};
+  st.m = -INFINITY;
+  st.l = 0.f;
   const int krow_a = sigma(l32);
 
   uint4 kr[C::kKChunks];
   uint4 vr[C::kKpt];
+  KIds kid{0, 0};
   if (ntiles > 0) {
-    const int kt0 = nfull > 0 ? flist[0] : plist[0];
-    P::load_tile(p, sb, s, h, kt0, nfull == 0, tid, kr, vr);
-    P::store_tile(smem, tid, kr, vr);
+    P::load_tile(p, sb, s, h, tile_of(0), nfull == 0, tid, kr, vr, kid);
+    P::store_tile(smem, tid, nfull == 0, kr, vr, kid);
   }
+  // Drain every outstanding load (the Q operand included) before the loops so
+  // that no wait for them is carried into a loop body.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const bool masked = t >= nfull;
-    const int kt = masked ? plist[t - nfull] : flist[t];
+  // FULL tiles: no mask code.  The tile after the current one is loaded into
+  // registers while the current one is used, then stored to the other buffer.
+  int t = 0;
+  for (; t < nfull; ++t) {
     const bool has_next = t + 1 < ntiles;
-    if (has_next) {
-      const bool mnext = t + 1 >= nfull;
-      const int ktn = mnext ? plist[t + 1 - nfull] : flist[t + 1];
-      P::load_tile(p, sb, s, h, ktn, mnext, tid, kr, vr);
-    }
-    const char* Ks = smem + (t & 1) * C::kStage;
-    const char* Vt = Ks + C::kKBuf;
-
-    // ---- S^T = K Q^T for the two 32-key blocks of the tile -------------
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(Ks + krow_a * C::kKP + (ks * 16 + g * 8) * 2);
-        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(Ks + (32 + krow_a) * C::kKP + (ks * 16 + g * 8) * 2);
-        s0 = mfma(k0, qf.v[ks], s0);
-        s1 = mfma(k1, qf.v[ks], s1);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < D / 8; ++c) {
-        const float4 k0 = *reinterpret_cast<const float4*>(Ks + krow_a * C::kKP + (g * (D / 2) + c * 4) * 4);
-        const float4 k1 = *reinterpret_cast<const float4*>(Ks + (32 + krow_a) * C::kKP + (g * (D / 2) + c * 4) * 4);
-        s0 = mfma(k0.x, qf.v[c * 4 + 0], s0);
-        s1 = mfma(k1.x, qf.v[c * 4 + 0], s1);
-        s0 = mfma(k0.y, qf.v[c * 4 + 1], s0);
-        s1 = mfma(k1.y, qf.v[c * 4 + 1], s1);
-        s0 = mfma(k0.z, qf.v[c * 4 + 2], s0);
-        s1 = mfma(k1.z, qf.v[c * 4 + 2], s1);
-        s0 = mfma(k0.w, qf.v[c * 4 + 3], s0);
-        s1 = mfma(k1.w, qf.v[c * 4 + 3], s1);
-      }
-    }
-
-    // ---- online softmax (base 2) ---------------------------------------
-    // Register r of block b holds key kt*64 + b*32 + 16*(r/8) + 8*g + r%8.
-    float x[32];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      x[r] = s0[r] * sl2;
-      x[16 + r] = s1[r] * sl2;
-    }
-    if (masked) {
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = kt * kBN + b * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
-          if (!visible(p.mask, sb, qi, qids, j)) x[b * 16 + r] = -INFINITY;
-        }
-      }
-    }
-    float mx = x[0];
-#pragma unroll
-    for (int r = 1; r < 32; ++r) mx = fmaxf(mx, x[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float rs = 0.f;
-#pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      x[r] = fast_exp2(x[r] - m_use);
-      rs += x[r];
-    }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int dt = 0; dt < C::kDT; ++dt) acc[dt] *= alpha;
-    }
-
-    // ---- acc^T += V^T P^T ------------------------------------------------
-    if constexpr (sizeof(T) == 2) {
-      bf16x8 pf[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        uint4 u;
-        u.x = pack_bf16x2(x[k * 8 + 0], x[k * 8 + 1]);
-        u.y = pack_bf16x2(x[k * 8 + 2], x[k * 8 + 3]);
-        u.z = pack_bf16x2(x[k * 8 + 4], x[k * 8 + 5]);
-        u.w = pack_bf16x2(x[k * 8 + 6], x[k * 8 + 7]);
-        pf[k] = __builtin_bit_cast(bf16x8, u);
-      }
-#pragma unroll
-      for (int dt = 0; dt < C::kDT; ++dt) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(Vt + (dt * 32 + l32) * C::kVP + (k * 16 + g * 8) * 2);
-          acc[dt] = mfma(vf, pf[k], acc[dt]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int dt = 0; dt < C::kDT; ++dt) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const char* src = Vt + (dt * 32 + l32) * C::kVP + (b * 32 + 16 * hh + 8 * g) * 4;
-            const float4 v0 = *reinterpret_cast<const float4*>(src);
-            const float4 v1 = *reinterpret_cast<const float4*>(src + 16);
-            const int r0 = b * 16 + hh * 8;
-            acc[dt] = mfma(v0.x, x[r0 + 0], acc[dt]);
-            acc[dt] = mfma(v0.y, x[r0 + 1], acc[dt]);
-            acc[dt] = mfma(v0.z, x[r0 + 2], acc[dt]);
-            acc[dt] = mfma(v0.w, x[r0 + 3], acc[dt]);
-            acc[dt] = mfma(v1.x, x[r0 + 4], acc[dt]);
-            acc[dt] = mfma(v1.y, x[r0 + 5], acc[dt]);
-            acc[dt] = mfma(v1.z, x[r0 + 6], acc[dt]);
-            acc[dt] = mfma(v1.w, x[r0 + 7], acc[dt]);
-          }
-        }
-      }
-    }
-
-    if (has_next) P::store_tile(smem + ((t + 1) & 1) * C::kStage, tid, kr, vr);
+    const bool mnext = t + 1 >= nfull;
+    if (has_next) P::load_tile(p, sb, s, h, tile_of(t + 1), mnext, tid, kr, vr, kid);
+    tile_step<T, D, false>(smem + (t & 1) * C::kStage, qf, st, p, sb, flist[t], qi, qids, g, l32,
+                           krow_a);
+    if (has_next) P::store_tile(smem + ((t + 1) & 1) * C::kStage, tid, mnext, kr, vr, kid);
+    __syncthreads();
+  }
+  // PARTIAL tiles: the element predicate, with the tile's key ids in LDS.
+  for (; t < ntiles; ++t) {
+    const bool has_next = t + 1 < ntiles;
+    if (has_next) P::load_tile(p, sb, s, h, plist[t + 1 - nfull], true, tid, kr, vr, kid);
+    tile_step<T, D, true>(smem + (t & 1) * C::kStage, qf, st, p, sb, plist[t - nfull], qi, qids, g,
+                          l32, krow_a);
+    if (has_next) P::store_tile(smem + ((t + 1) & 1) * C::kStage, tid, true, kr, vr, kid);
     __syncthreads();
   }
 
   // ---- epilogue: O = acc / l, LSE = m + ln(l) ------------------------------
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = st.l + __shfl_xor(st.l, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qvalid) {
     char* orow = static_cast<char*>(p.o) + ((sb.q0 + qi) * p.o_st + (int64_t)h * p.o_sh) * C::kElem;
@@ -383,8 +435,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(FwdDev p) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int d0 = dt * 32 + 8 * a4 + 4 * g;
-        const float o0 = acc[dt][a4 * 4 + 0] * inv, o1 = acc[dt][a4 * 4 + 1] * inv;
-        const float o2 = acc[dt][a4 * 4 + 2] * inv, o3 = acc[dt][a4 * 4 + 3] * inv;
+        const float o0 = st.acc[dt][a4 * 4 + 0] * inv, o1 = st.acc[dt][a4 * 4 + 1] * inv;
+        const float o2 = st.acc[dt][a4 * 4 + 2] * inv, o3 = st.acc[dt][a4 * 4 + 3] * inv;
         if constexpr (sizeof(T) == 2) {
           *reinterpret_cast<uint2*>(orow + d0 * 2) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
         } else {
@@ -393,7 +445,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(FwdDev p) {
       }
     }
     if (g == 0 && p.lse != nullptr) {
-      const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      const float lse = l_tot > 0.f ? (st.m + __log2f(l_tot)) * kLn2 : -INFINITY;
       p.lse[(int64_t)h * p.lse_sh + sb.q0 + qi] = lse;
     }
   }

@@ -42,7 +42,8 @@ struct FwdDev {
   const int32_t* block_table;
   int64_t bt_stride, num_pages;
   int32_t page_size;
-  float scale_log2;  // softmax scale times log2(e)
+  int32_t page_shift;  // log2(page_size) for a power of two, else -1
+  float scale_log2;    // softmax scale times log2(e)
   // decode split-KV
   float* ws;             // [n_rows, splits, H, D + 2] partial results
   int32_t split_tiles;   // kv tiles per split
@@ -59,6 +60,14 @@ hipError_t launch_paged_gather(const MaskDev& m, int32_t max_lk, const void* poo
                                int64_t st_head, int32_t elem_bytes, int32_t H, int32_t D,
                                int32_t page_size, int64_t num_pages, const int32_t* block_table,
                                int64_t bt_stride, void* out, hipStream_t st);
+
+// log2 of a power-of-two page size, else -1.
+inline int32_t page_shift_of(int32_t page_size) {
+  if (page_size < 1 || (page_size & (page_size - 1)) != 0) return -1;
+  int32_t s = 0;
+  while ((1 << s) < page_size) ++s;
+  return s;
+}
 
 // Forward kernels.  Return hipErrorInvalidValue for a combination that is
 // not compiled (the caller checks support first).

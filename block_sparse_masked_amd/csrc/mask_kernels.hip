@@ -244,6 +244,10 @@ __global__ __launch_bounds__(kThreads) void validate_kernel(MaskDev m, int32_t m
   }
 }
 
+__device__ __forceinline__ int32_t page_shift_of_dev(int32_t page_size) {
+  return (page_size & (page_size - 1)) == 0 ? __builtin_ctz((uint32_t)page_size) : -1;
+}
+
 // Copies 16-byte chunks of every (key, head) row from the pool to the
 // contiguous output through paged_row, the forward's own addressing.
 __global__ __launch_bounds__(kThreads) void paged_gather_kernel(
@@ -259,7 +263,8 @@ __global__ __launch_bounds__(kThreads) void paged_gather_kernel(
   const int h = rem / chunks, c = rem % chunks;
   const SeqBounds b = seq_bounds(m, s, 1 << 30, max_lk);
   if (j >= b.lk) return;  // the ragged tail is masked: no read, no write
-  const int64_t prow = paged_row(bt, bt_stride, s, j, page_size, num_pages);
+  const int64_t prow = paged_row(bt, bt_stride, s, j, page_size, page_shift_of_dev(page_size),
+                                 num_pages);
   const uint4 v = *reinterpret_cast<const uint4*>(pool + prow * st_tok_b + h * st_head_b + c * 16);
   *reinterpret_cast<uint4*>(out + ((b.k0 + j) * H + h) * (int64_t)row_bytes + c * 16) = v;
 }
