@@ -39,6 +39,7 @@ constexpr int kBM = 128;
 constexpr int kBN = 64;
 constexpr int kThreads = 256;
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRescaleSlack = 8.0f;
 
 template <typename T, int D>
 struct Cfg {
@@ -72,109 +73,148 @@ __device__ __forceinline__ int sigma(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Dword i of a 16-byte chunk.
+__device__ __forceinline__ uint32_t dword(const uint4& v, int i) {
+  return __builtin_bit_cast(u32x4, v)[i];
+}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bf16 (round to nearest even) in one dword, lo first.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = static_cast<__bf16>(lo);
-  __bf16 b = static_cast<__bf16>(hi);
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
 template <typename T, int D, bool PAGED>
 struct Prefill {
   using C = Cfg<T, D>;
 
-  // Global -> registers for one kv tile.  Rows past the sequence (only in
-  // PARTIAL tiles) are zero and never read.
-  static __device__ __forceinline__ void load_tile(const FwdDev& p, const SeqBounds& sb, int s,
-                                                   int h, int kt, bool masked, int tid,
-                                                   uint4 (&kr)[C::kKChunks],
-                                                   uint4 (&vr)[C::kKpt], KIds& kid) {
-    if (masked && tid < kBN) kid = load_kids(p.mask, sb, kt * kBN + tid);
-    const char* kb = static_cast<const char*>(p.k) + (int64_t)h * p.k_sh * C::kElem;
-    const char* vb = static_cast<const char*>(p.v) + (int64_t)h * p.v_sh * C::kElem;
-    // Physical rows first (block-table reads all in flight together), then
-    // the tile loads.  Rows past the sequence are marked -1.
-    int64_t krows[C::kKChunks], vrows[C::kKpt];
+  // Per-thread byte offsets of the first K row and first V row this thread
+  // stages, relative to the first key of the tile (contiguous K/V); the other
+  // rows follow at uniform strides.  Computed once per workgroup.
+  struct Offsets {
+    uint32_t k, v;
+  };
+  static __device__ __forceinline__ Offsets offsets(const FwdDev& p, int tid) {
     const int ch = tid % C::kCh, kg = tid / C::kCh;
-    if constexpr (PAGED) {
-      int32_t kpe[C::kKChunks], vpe[C::kKpt];
+    return Offsets{(uint32_t)((tid / C::kCh) * p.k_st * C::kElem + ch * 16),
+                   (uint32_t)(kg * C::kKpt * p.v_st * C::kElem + ch * 16)};
+  }
+
+  // Global -> registers, K rows of one kv tile.  MASKED (PARTIAL) tiles leave
+  // rows past the sequence zero and never read them.
+  template <bool MASKED>
+  static __device__ __forceinline__ void load_k(const FwdDev& p, const SeqBounds& sb, int s, int h,
+                                                int kt, int tid, const Offsets& off,
+                                                uint4 (&kr)[C::kKChunks]) {
+    const int ch = tid % C::kCh;
+    if constexpr (!PAGED) {
+      const char* kb = static_cast<const char*>(p.k) +
+                       ((sb.k0 + (int64_t)kt * kBN) * p.k_st + (int64_t)h * p.k_sh) * C::kElem;
+#pragma unroll
+      for (int u = 0; u < C::kKChunks; ++u) {
+        const int j = kt * kBN + (tid + kThreads * u) / C::kCh;
+        const uint32_t o = off.k + (uint32_t)(u * (kThreads / C::kCh) * p.k_st * C::kElem);
+        kr[u] = (!MASKED || j < sb.lk) ? *reinterpret_cast<const uint4*>(kb + o)
+                                       : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+      // Paged: all block-table entries first, then the loads.
+      const char* kb = static_cast<const char*>(p.k) + (int64_t)h * p.k_sh * C::kElem;
+      int32_t pe[C::kKChunks];
 #pragma unroll
       for (int u = 0; u < C::kKChunks; ++u) {
         const int j = min(kt * kBN + (tid + kThreads * u) / C::kCh, sb.lk - 1);
-        kpe[u] = page_entry(p.block_table, p.bt_stride, s, j, p.page_size, p.page_shift);
-      }
-#pragma unroll
-      for (int u = 0; u < C::kKpt; ++u) {
-        const int j = min(kt * kBN + kg * C::kKpt + u, sb.lk - 1);
-        vpe[u] = page_entry(p.block_table, p.bt_stride, s, j, p.page_size, p.page_shift);
+        pe[u] = page_entry(p.block_table, p.bt_stride, s, j, p.page_size, p.page_shift);
       }
 #pragma unroll
       for (int u = 0; u < C::kKChunks; ++u) {
         const int j = kt * kBN + (tid + kThreads * u) / C::kCh;
-        krows[u] = (!masked || j < sb.lk) ? row_in_page(kpe[u], j, p.page_size, p.page_shift, p.num_pages) : -1;
+        const int64_t r = row_in_page(pe[u], j, p.page_size, p.page_shift, p.num_pages);
+        kr[u] = (!MASKED || j < sb.lk)
+                    ? *reinterpret_cast<const uint4*>(kb + r * p.k_st * C::kElem + ch * 16)
+                    : make_uint4(0, 0, 0, 0);
       }
-#pragma unroll
-      for (int u = 0; u < C::kKpt; ++u) {
-        const int j = kt * kBN + kg * C::kKpt + u;
-        vrows[u] = (!masked || j < sb.lk) ? row_in_page(vpe[u], j, p.page_size, p.page_shift, p.num_pages) : -1;
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < C::kKChunks; ++u) {
-        const int j = kt * kBN + (tid + kThreads * u) / C::kCh;
-        krows[u] = (!masked || j < sb.lk) ? sb.k0 + j : -1;
-      }
-#pragma unroll
-      for (int u = 0; u < C::kKpt; ++u) {
-        const int j = kt * kBN + kg * C::kKpt + u;
-        vrows[u] = (!masked || j < sb.lk) ? sb.k0 + j : -1;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < C::kKChunks; ++u) {
-      const int kch = (tid + kThreads * u) % C::kCh;
-      kr[u] = krows[u] >= 0 ? *reinterpret_cast<const uint4*>(kb + krows[u] * p.k_st * C::kElem + kch * 16)
-                            : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < C::kKpt; ++u) {
-      vr[u] = vrows[u] >= 0 ? *reinterpret_cast<const uint4*>(vb + vrows[u] * p.v_st * C::kElem + ch * 16)
-                            : make_uint4(0, 0, 0, 0);
     }
   }
 
-  // Registers -> LDS: K row-major, V transposed (V^T[d][key]).
-  static __device__ __forceinline__ void store_tile(char* stage, int tid, bool masked,
-                                                    const uint4 (&kr)[C::kKChunks],
-                                                    const uint4 (&vr)[C::kKpt], const KIds& kid) {
-    if (masked && tid < kBN) {
-      int32_t* ids = reinterpret_cast<int32_t*>(stage + C::kKBuf + C::kVBuf);
-      ids[tid] = kid.a;
-      ids[kBN + tid] = kid.b;
+  // Global -> registers, V rows (and, for MASKED tiles, the key ids).
+  template <bool MASKED>
+  static __device__ __forceinline__ void load_v(const FwdDev& p, const SeqBounds& sb, int s, int h,
+                                                int kt, int tid, const Offsets& off,
+                                                uint4 (&vr)[C::kKpt], KIds& kid) {
+    if (MASKED && tid < kBN) kid = load_kids(p.mask, sb, kt * kBN + tid);
+    const int ch = tid % C::kCh, kg = tid / C::kCh;
+    if constexpr (!PAGED) {
+      const char* vb = static_cast<const char*>(p.v) +
+                       ((sb.k0 + (int64_t)kt * kBN) * p.v_st + (int64_t)h * p.v_sh) * C::kElem;
+#pragma unroll
+      for (int u = 0; u < C::kKpt; ++u) {
+        const int j = kt * kBN + kg * C::kKpt + u;
+        const uint32_t o = off.v + (uint32_t)(u * p.v_st * C::kElem);
+        vr[u] = (!MASKED || j < sb.lk) ? *reinterpret_cast<const uint4*>(vb + o)
+                                       : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+      const char* vb = static_cast<const char*>(p.v) + (int64_t)h * p.v_sh * C::kElem;
+      int32_t pe[C::kKpt];
+#pragma unroll
+      for (int u = 0; u < C::kKpt; ++u) {
+        const int j = min(kt * kBN + kg * C::kKpt + u, sb.lk - 1);
+        pe[u] = page_entry(p.block_table, p.bt_stride, s, j, p.page_size, p.page_shift);
+      }
+#pragma unroll
+      for (int u = 0; u < C::kKpt; ++u) {
+        const int j = kt * kBN + kg * C::kKpt + u;
+        const int64_t r = row_in_page(pe[u], j, p.page_size, p.page_shift, p.num_pages);
+        vr[u] = (!MASKED || j < sb.lk)
+                    ? *reinterpret_cast<const uint4*>(vb + r * p.v_st * C::kElem + ch * 16)
+                    : make_uint4(0, 0, 0, 0);
+      }
     }
+  }
+
+  // Registers -> LDS, K row-major.
+  static __device__ __forceinline__ void store_k(char* stage, int tid,
+                                                 const uint4 (&kr)[C::kKChunks]) {
 #pragma unroll
     for (int u = 0; u < C::kKChunks; ++u) {
       const int c = tid + kThreads * u;
       const int row = c / C::kCh, ch = c % C::kCh;
       *reinterpret_cast<uint4*>(stage + row * C::kKP + ch * 16) = kr[u];
     }
+  }
+
+  // Registers -> LDS, V transposed (V^T[d][key]) and the key ids.
+  static __device__ __forceinline__ void store_v(char* stage, int tid, bool masked,
+                                                 const uint4 (&vr)[C::kKpt], const KIds& kid) {
+    if (masked && tid < kBN) {
+      int32_t* ids = reinterpret_cast<int32_t*>(stage + C::kKBuf + C::kVBuf);
+      ids[tid] = kid.a;
+      ids[kBN + tid] = kid.b;
+    }
     char* vt = stage + C::kKBuf;
     const int ch = tid % C::kCh, kg = tid / C::kCh;
     if constexpr (sizeof(T) == 2) {
-      const uint32_t* w[C::kKpt];
+      // Dword i of key u holds d = 2i (low half) and 2i+1 (high half); pack
+      // the same d of consecutive keys into one dword with v_perm.
 #pragma unroll
-      for (int u = 0; u < C::kKpt; ++u) w[u] = reinterpret_cast<const uint32_t*>(&vr[u]);
-#pragma unroll
-      for (int e = 0; e < C::kEpc; ++e) {
-        const int d = ch * C::kEpc + e;
-        const int sh = (e & 1) * 16;
-        uint32_t h16[C::kKpt];
-#pragma unroll
-        for (int u = 0; u < C::kKpt; ++u) h16[u] = (w[u][e >> 1] >> sh) & 0xffffu;
-        char* dst = vt + d * C::kVP + kg * C::kKpt * 2;
+      for (int i = 0; i < C::kEpc / 2; ++i) {
+        const uint32_t w0 = dword(vr[0], i), w1 = dword(vr[1], i);
+        const uint32_t lo01 = __builtin_amdgcn_perm(w1, w0, 0x05040100u);
+        const uint32_t hi01 = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
+        char* d0 = vt + (ch * C::kEpc + 2 * i) * C::kVP + kg * C::kKpt * 2;
         if constexpr (C::kKpt == 4) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(h16[0] | (h16[1] << 16), h16[2] | (h16[3] << 16));
+          const uint32_t w2 = dword(vr[2], i), w3 = dword(vr[3], i);
+          const uint32_t lo23 = __builtin_amdgcn_perm(w3, w2, 0x05040100u);
+          const uint32_t hi23 = __builtin_amdgcn_perm(w3, w2, 0x07060302u);
+          *reinterpret_cast<uint2*>(d0) = make_uint2(lo01, lo23);
+          *reinterpret_cast<uint2*>(d0 + C::kVP) = make_uint2(hi01, hi23);
         } else {
-          *reinterpret_cast<uint32_t*>(dst) = h16[0] | (h16[1] << 16);
+          *reinterpret_cast<uint32_t*>(d0) = lo01;
+          *reinterpret_cast<uint32_t*>(d0 + C::kVP) = hi01;
         }
       }
     } else {
@@ -185,11 +225,8 @@ struct Prefill {
         char* dst = vt + d * C::kVP + kg * C::kKpt * 4;
 #pragma unroll
         for (int u0 = 0; u0 < C::kKpt; u0 += 4) {
-          const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vr[u0 + 0]);
-          const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vr[u0 + 1]);
-          const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vr[u0 + 2]);
-          const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vr[u0 + 3]);
-          *reinterpret_cast<uint4*>(dst + u0 * 4) = make_uint4(w0[e], w1[e], w2[e], w3[e]);
+          *reinterpret_cast<uint4*>(dst + u0 * 4) =
+              make_uint4(dword(vr[u0 + 0], e), dword(vr[u0 + 1], e), dword(vr[u0 + 2], e), dword(vr[u0 + 3], e));
         }
       }
     }
@@ -216,15 +253,13 @@ struct RowState {
   float m, l;          // running max (base-2 scaled) and this lane's partial sum
 };
 
-// One kv tile: S^T = K Q^T, the element mask on PARTIAL tiles, the online
-// softmax update and acc^T += V^T P^T.
-template <typename T, int D, bool MASKED>
-__device__ __forceinline__ void tile_step(const char* Ks, const QFrag<T, D>& qf, RowState<D>& st,
-                                          const FwdDev& p, const SeqBounds& sb, int kt, int qi,
-                                          QIds qids, int g, int l32, int krow_a) {
+// Phase 1 of a kv tile: S^T = K Q^T for the tile's two 32-key blocks.
+template <typename T, int D>
+__device__ __forceinline__ void s_product(const char* Ks, const QFrag<T, D>& qf, int g, int krow_a,
+                                          f32x16& s0, f32x16& s1) {
   using C = Cfg<T, D>;
-  const char* Vt = Ks + C::kKBuf;
-  f32x16 s0 = f32x16{}, s1 = f32x16{};
+  s0 = f32x16{};
+  s1 = f32x16{};
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
@@ -248,17 +283,30 @@ __device__ __forceinline__ void tile_step(const char* Ks, const QFrag<T, D>& qf,
       s1 = mfma(k1.w, qf.v[c * 4 + 3], s1);
     }
   }
+}
 
-  // Register r of block b holds key kt*64 + b*32 + 16*(r/8) + 8*g + r%8.
-  float x[32];
-  const float sl2 = p.scale_log2;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    x[r] = s0[r] * sl2;
-    x[16 + r] = s1[r] * sl2;
-  }
+// Phase 2: the element mask (PARTIAL tiles), the online-softmax update and
+// the probabilities in x (overwritten in place).
+// Register r of block b holds key kt*64 + b*32 + 16*(r/8) + 8*g + r%8.
+// Scores stay unscaled until the exponent: max(s * c) = c * max(s) for the
+// positive scale c, and exp2(s * c - m) is one fma and one exp.
+template <typename T, int D, bool MASKED>
+__device__ __forceinline__ void softmax_update(f32x16& s0, f32x16& s1, RowState<D>& st,
+                                               const char* Ks, const FwdDev& p,
+                                               const SeqBounds& sb, int kt, int qi, QIds qids,
+                                               int g) {
+  using C = Cfg<T, D>;
   if constexpr (MASKED) {
+    // The predicate is applied on a plain array copy: conditional element
+    // stores through a reference to the MFMA result vector were not kept by
+    // the compiler.
     const int32_t* ids = reinterpret_cast<const int32_t*>(Ks + C::kKBuf + C::kVBuf);
+    float x[32];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      x[r] = s0[r];
+      x[16 + r] = s1[r];
+    }
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
@@ -268,36 +316,72 @@ __device__ __forceinline__ void tile_step(const char* Ks, const QFrag<T, D>& qf,
         if (!visible_ids(p.mask, sb, qi, qids, kt * kBN + jj, kid)) x[b * 16 + r] = -INFINITY;
       }
     }
-  }
-  float mx = x[0];
 #pragma unroll
-  for (int r = 1; r < 32; ++r) mx = fmaxf(mx, x[r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(st.m, mx);
-  const float m_use = (MASKED && m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = fast_exp2(st.m - m_use);
-  float rs = 0.f;
-#pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    x[r] = fast_exp2(x[r] - m_use);
-    rs += x[r];
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = x[r];
+      s1[r] = x[16 + r];
+    }
   }
-  st.l = st.l * alpha + rs;
-  st.m = m_new;
-  if (__ballot(alpha != 1.f)) {
+  const float sl2 = p.scale_log2;
+  float mx = s0[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+  // Lazy rescaling: the reference max st.m moves only when the tile's max
+  // exceeds it by more than kRescaleSlack (log2 units), or when it is still
+  // -inf.  exp2(s - m_ref) then stays below 2^kRescaleSlack, and O = acc / l
+  // is the same quantity for any reference, so skipping the rescale of acc
+  // changes only rounding.  The decision is per wave so acc is rescaled in a
+  // wave-uniform branch.
+  const bool grow = !(mx <= st.m + kRescaleSlack);
+  float m_ref = st.m;
+  if (__ballot(grow)) {
+    const float m_new = fmaxf(st.m, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(st.m - m_use);
+    st.l *= alpha;
 #pragma unroll
     for (int dt = 0; dt < C::kDT; ++dt) st.acc[dt] *= alpha;
+    st.m = m_new;
+    m_ref = m_use;
   }
+  // A row with nothing visible so far keeps -inf; its exponents use 0 so that
+  // masked scores give exp2(-inf) = 0, never -inf + inf.
+  if constexpr (MASKED) m_ref = (m_ref == -INFINITY) ? 0.f : m_ref;
+  float rs = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s0[r] = fast_exp2(fmaf(s0[r], sl2, -m_ref));
+    rs += s0[r];
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s1[r] = fast_exp2(fmaf(s1[r], sl2, -m_ref));
+    rs += s1[r];
+  }
+  st.l += rs;
+}
 
+// Phase 3: acc^T += V^T P^T; p0/p1 hold the probabilities of the two
+// 32-key blocks in the accumulator layout of the S product.
+template <typename T, int D>
+__device__ __forceinline__ void pv_product(const char* Ks, const f32x16& p0, const f32x16& p1,
+                                           RowState<D>& st, int g, int l32) {
+  using C = Cfg<T, D>;
+  const char* Vt = Ks + C::kKBuf;
   if constexpr (sizeof(T) == 2) {
     bf16x8 pf[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
+      const f32x16& src = (k < 2) ? p0 : p1;
+      const int r0 = (k & 1) * 8;
       uint4 u;
-      u.x = pack_bf16x2(x[k * 8 + 0], x[k * 8 + 1]);
-      u.y = pack_bf16x2(x[k * 8 + 2], x[k * 8 + 3]);
-      u.z = pack_bf16x2(x[k * 8 + 4], x[k * 8 + 5]);
-      u.w = pack_bf16x2(x[k * 8 + 6], x[k * 8 + 7]);
+      u.x = pack_bf16x2(src[r0 + 0], src[r0 + 1]);
+      u.y = pack_bf16x2(src[r0 + 2], src[r0 + 3]);
+      u.z = pack_bf16x2(src[r0 + 4], src[r0 + 5]);
+      u.w = pack_bf16x2(src[r0 + 6], src[r0 + 7]);
       pf[k] = __builtin_bit_cast(bf16x8, u);
     }
 #pragma unroll
@@ -311,22 +395,23 @@ __device__ __forceinline__ void tile_step(const char* Ks, const QFrag<T, D>& qf,
   } else {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
+      const f32x16& src = b == 0 ? p0 : p1;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
         for (int dt = 0; dt < C::kDT; ++dt) {
-          const char* src = Vt + (dt * 32 + l32) * C::kVP + (b * 32 + 16 * hh + 8 * g) * 4;
-          const float4 v0 = *reinterpret_cast<const float4*>(src);
-          const float4 v1 = *reinterpret_cast<const float4*>(src + 16);
-          const int r0 = b * 16 + hh * 8;
-          st.acc[dt] = mfma(v0.x, x[r0 + 0], st.acc[dt]);
-          st.acc[dt] = mfma(v0.y, x[r0 + 1], st.acc[dt]);
-          st.acc[dt] = mfma(v0.z, x[r0 + 2], st.acc[dt]);
-          st.acc[dt] = mfma(v0.w, x[r0 + 3], st.acc[dt]);
-          st.acc[dt] = mfma(v1.x, x[r0 + 4], st.acc[dt]);
-          st.acc[dt] = mfma(v1.y, x[r0 + 5], st.acc[dt]);
-          st.acc[dt] = mfma(v1.z, x[r0 + 6], st.acc[dt]);
-          st.acc[dt] = mfma(v1.w, x[r0 + 7], st.acc[dt]);
+          const char* vs = Vt + (dt * 32 + l32) * C::kVP + (b * 32 + 16 * hh + 8 * g) * 4;
+          const float4 v0 = *reinterpret_cast<const float4*>(vs);
+          const float4 v1 = *reinterpret_cast<const float4*>(vs + 16);
+          const int r0 = hh * 8;
+          st.acc[dt] = mfma(v0.x, src[r0 + 0], st.acc[dt]);
+          st.acc[dt] = mfma(v0.y, src[r0 + 1], st.acc[dt]);
+          st.acc[dt] = mfma(v0.z, src[r0 + 2], st.acc[dt]);
+          st.acc[dt] = mfma(v0.w, src[r0 + 3], st.acc[dt]);
+          st.acc[dt] = mfma(v1.x, src[r0 + 4], st.acc[dt]);
+          st.acc[dt] = mfma(v1.y, src[r0 + 5], st.acc[dt]);
+          st.acc[dt] = mfma(v1.z, src[r0 + 6], st.acc[dt]);
+          st.acc[dt] = mfma(v1.w, src[r0 + 7], st.acc[dt]);
         }
       }
     }
@@ -353,7 +438,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(FwdDev p) {
   const int ntiles = nfull + p.part_cnt[row];
   const int32_t* flist = p.full_idx + (int64_t)row * p.n_kt;
   const int32_t* plist = p.part_idx + (int64_t)row * p.n_kt;
-  auto tile_of = [&](int t) { return t < nfull ? flist[t] : plist[t - nfull]; };
 
   const int qi = a * kBM + wave * 32 + l32;  // query row inside the sequence
   const bool qvalid = qi < sb.lq;
@@ -394,34 +478,65 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(FwdDev p) {
   uint4 kr[C::kKChunks];
   uint4 vr[C::kKpt];
   KIds kid{0, 0};
+  const typename P::Offsets off = P::offsets(p, tid);
   if (ntiles > 0) {
-    P::load_tile(p, sb, s, h, tile_of(0), nfull == 0, tid, kr, vr, kid);
-    P::store_tile(smem, tid, nfull == 0, kr, vr, kid);
+    if (nfull > 0) {
+      P::template load_k<false>(p, sb, s, h, flist[0], tid, off, kr);
+      P::template load_v<false>(p, sb, s, h, flist[0], tid, off, vr, kid);
+    } else {
+      P::template load_k<true>(p, sb, s, h, plist[0], tid, off, kr);
+      P::template load_v<true>(p, sb, s, h, plist[0], tid, off, vr, kid);
+    }
+    P::store_k(smem, tid, kr);
+    P::store_v(smem, tid, nfull == 0, vr, kid);
   }
   // Drain every outstanding load (the Q operand included) before the loops so
   // that no wait for them is carried into a loop body.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // FULL tiles: no mask code.  The tile after the current one is loaded into
-  // registers while the current one is used, then stored to the other buffer.
+  // Each iteration uses tile t from one LDS buffer and stages tile t+1 into
+  // the other: K(t+1) is loaded before the S product and stored after the
+  // softmax, V(t+1) is loaded after the S product and stored after the P V
+  // product, so at most one operand's staging registers are live at a time.
+  // FULL tiles: no mask code.
   int t = 0;
   for (; t < nfull; ++t) {
     const bool has_next = t + 1 < ntiles;
     const bool mnext = t + 1 >= nfull;
-    if (has_next) P::load_tile(p, sb, s, h, tile_of(t + 1), mnext, tid, kr, vr, kid);
-    tile_step<T, D, false>(smem + (t & 1) * C::kStage, qf, st, p, sb, flist[t], qi, qids, g, l32,
-                           krow_a);
-    if (has_next) P::store_tile(smem + ((t + 1) & 1) * C::kStage, tid, mnext, kr, vr, kid);
+    const int ktn = has_next ? (mnext ? plist[0] : flist[t + 1]) : 0;
+    char* cur = smem + (t & 1) * C::kStage;
+    char* nxt = smem + ((t + 1) & 1) * C::kStage;
+    if (has_next) {
+      if (mnext) P::template load_k<true>(p, sb, s, h, ktn, tid, off, kr);
+      else P::template load_k<false>(p, sb, s, h, ktn, tid, off, kr);
+    }
+    f32x16 s0, s1;
+    s_product<T, D>(cur, qf, g, krow_a, s0, s1);
+    if (has_next) {
+      if (mnext) P::template load_v<true>(p, sb, s, h, ktn, tid, off, vr, kid);
+      else P::template load_v<false>(p, sb, s, h, ktn, tid, off, vr, kid);
+    }
+    softmax_update<T, D, false>(s0, s1, st, cur, p, sb, flist[t], qi, qids, g);
+    if (has_next) P::store_k(nxt, tid, kr);
+    pv_product<T, D>(cur, s0, s1, st, g, l32);
+    if (has_next) P::store_v(nxt, tid, mnext, vr, kid);
     __syncthreads();
   }
   // PARTIAL tiles: the element predicate, with the tile's key ids in LDS.
   for (; t < ntiles; ++t) {
     const bool has_next = t + 1 < ntiles;
-    if (has_next) P::load_tile(p, sb, s, h, plist[t + 1 - nfull], true, tid, kr, vr, kid);
-    tile_step<T, D, true>(smem + (t & 1) * C::kStage, qf, st, p, sb, plist[t - nfull], qi, qids, g,
-                          l32, krow_a);
-    if (has_next) P::store_tile(smem + ((t + 1) & 1) * C::kStage, tid, true, kr, vr, kid);
+    const int ktn = has_next ? plist[t + 1 - nfull] : 0;
+    char* cur = smem + (t & 1) * C::kStage;
+    char* nxt = smem + ((t + 1) & 1) * C::kStage;
+    if (has_next) P::template load_k<true>(p, sb, s, h, ktn, tid, off, kr);
+    f32x16 s0, s1;
+    s_product<T, D>(cur, qf, g, krow_a, s0, s1);
+    if (has_next) P::template load_v<true>(p, sb, s, h, ktn, tid, off, vr, kid);
+    softmax_update<T, D, true>(s0, s1, st, cur, p, sb, plist[t - nfull], qi, qids, g);
+    if (has_next) P::store_k(nxt, tid, kr);
+    pv_product<T, D>(cur, s0, s1, st, g, l32);
+    if (has_next) P::store_v(nxt, tid, true, vr, kid);
     __syncthreads();
   }
 
