@@ -89,15 +89,26 @@ __device__ __forceinline__ KIds load_kids(const MaskDev& m, const SeqBounds& b, 
 // Element predicate: is key j of the sequence visible to its query row i?
 // Query row i sits at position lk - lq + i; the causal condition keeps the
 // diagonal (j <= position).  Pairs outside the sequence are not visible.
-// kid holds key j's ids (load_kids).
+// kid holds key j's ids (load_kids).  Branch-free, one instance per kind.
+template <int KIND>
+__device__ __forceinline__ bool visible_k(const MaskDev& m, const SeqBounds& b, int i, QIds qi,
+                                          int j, KIds kid) {
+  const bool in = (i < b.lq) & (j < b.lk);
+  if constexpr (KIND == BMATTN_MASK_FULL) return in;
+  const bool causal = in & (j <= b.lk - b.lq + i);
+  if constexpr (KIND == BMATTN_MASK_CAUSAL) return causal;
+  if constexpr (KIND == BMATTN_MASK_SHARED_PREFIX) return causal & ((kid.a == 0) | (kid.a == qi.seg));
+  return causal & !((kid.a == m.think_role) & (kid.b < qi.turn));  // STRIP_THINKING
+}
+
 __device__ __forceinline__ bool visible_ids(const MaskDev& m, const SeqBounds& b, int i, QIds qi,
                                             int j, KIds kid) {
-  if (i >= b.lq || j >= b.lk) return false;
-  if (m.kind == BMATTN_MASK_FULL) return true;
-  if (j > b.lk - b.lq + i) return false;
-  if (m.kind == BMATTN_MASK_SHARED_PREFIX) return kid.a == 0 || kid.a == qi.seg;
-  if (m.kind == BMATTN_MASK_STRIP_THINKING) return !(kid.a == m.think_role && kid.b < qi.turn);
-  return true;  // CAUSAL
+  switch (m.kind) {
+    case BMATTN_MASK_FULL: return visible_k<BMATTN_MASK_FULL>(m, b, i, qi, j, kid);
+    case BMATTN_MASK_CAUSAL: return visible_k<BMATTN_MASK_CAUSAL>(m, b, i, qi, j, kid);
+    case BMATTN_MASK_SHARED_PREFIX: return visible_k<BMATTN_MASK_SHARED_PREFIX>(m, b, i, qi, j, kid);
+    default: return visible_k<BMATTN_MASK_STRIP_THINKING>(m, b, i, qi, j, kid);
+  }
 }
 
 __device__ __forceinline__ bool visible(const MaskDev& m, const SeqBounds& b, int i, QIds qi,

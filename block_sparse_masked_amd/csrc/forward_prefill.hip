@@ -285,6 +285,28 @@ __device__ __forceinline__ void s_product(const char* Ks, const QFrag<T, D>& qf,
   }
 }
 
+// The element predicate on one tile's scores (lane layout of the S product):
+// hidden pairs become -inf.  Key ids of the tile come from LDS.
+template <typename T, int D, int KIND>
+__device__ __forceinline__ void mask_scores(float (&x)[32], const char* Ks, const FwdDev& p,
+                                            const SeqBounds& sb, int kt, int qi, QIds qids,
+                                            int g) {
+  using C = Cfg<T, D>;
+  const int32_t* ids = reinterpret_cast<const int32_t*>(Ks + C::kKBuf + C::kVBuf);
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int jj = b * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
+      KIds kid{0, 0};
+      if constexpr (KIND == BMATTN_MASK_SHARED_PREFIX || KIND == BMATTN_MASK_STRIP_THINKING)
+        kid = KIds{ids[jj], ids[kBN + jj]};
+      x[b * 16 + r] = visible_k<KIND>(p.mask, sb, qi, qids, kt * kBN + jj, kid) ? x[b * 16 + r]
+                                                                               : -INFINITY;
+    }
+  }
+}
+
 // Phase 2: the element mask (PARTIAL tiles), the online-softmax update and
 // the probabilities in x (overwritten in place).
 // Register r of block b holds key kt*64 + b*32 + 16*(r/8) + 8*g + r%8.
@@ -299,22 +321,20 @@ __device__ __forceinline__ void softmax_update(f32x16& s0, f32x16& s1, RowState<
   if constexpr (MASKED) {
     // The predicate is applied on a plain array copy: conditional element
     // stores through a reference to the MFMA result vector were not kept by
-    // the compiler.
-    const int32_t* ids = reinterpret_cast<const int32_t*>(Ks + C::kKBuf + C::kVBuf);
+    // the compiler.  One straight-line instance per mask kind.
     float x[32];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       x[r] = s0[r];
       x[16 + r] = s1[r];
     }
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int jj = b * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
-        const KIds kid{ids[jj], ids[kBN + jj]};
-        if (!visible_ids(p.mask, sb, qi, qids, kt * kBN + jj, kid)) x[b * 16 + r] = -INFINITY;
-      }
+    switch (p.mask.kind) {
+      case BMATTN_MASK_FULL: mask_scores<T, D, BMATTN_MASK_FULL>(x, Ks, p, sb, kt, qi, qids, g); break;
+      case BMATTN_MASK_CAUSAL: mask_scores<T, D, BMATTN_MASK_CAUSAL>(x, Ks, p, sb, kt, qi, qids, g); break;
+      case BMATTN_MASK_SHARED_PREFIX:
+        mask_scores<T, D, BMATTN_MASK_SHARED_PREFIX>(x, Ks, p, sb, kt, qi, qids, g);
+        break;
+      default: mask_scores<T, D, BMATTN_MASK_STRIP_THINKING>(x, Ks, p, sb, kt, qi, qids, g); break;
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -418,19 +438,65 @@ __device__ __forceinline__ void pv_product(const char* Ks, const f32x16& p0, con
   }
 }
 
-template <typename T, int D, bool PAGED>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(FwdDev p) {
+// One kv tile for one wave group: the S product, softmax and P V product of
+// tile kt from LDS stage `cur`, with the group's next tile (ktn) staged into
+// `nxt`.  K(next) is loaded before the S product and stored after the
+// softmax; V(next) is loaded after the S product and stored after the P V
+// product, so at most one operand's staging registers are live at a time.
+template <typename T, int D, bool PAGED, bool MASKED>
+__device__ __forceinline__ void kv_step(const char* cur, char* nxt, bool has_next, bool mnext,
+                                        int ktn, int kt, const FwdDev& p, const SeqBounds& sb,
+                                        int s, int h, int gtid,
+                                        const typename Prefill<T, D, PAGED>::Offsets& off,
+                                        uint4 (&kr)[Cfg<T, D>::kKChunks],
+                                        uint4 (&vr)[Cfg<T, D>::kKpt], KIds& kid,
+                                        const QFrag<T, D>& qf, RowState<D>& st, int qi, QIds qids,
+                                        int g, int l32, int krow_a) {
+  using P = Prefill<T, D, PAGED>;
+  mnext = MASKED || mnext;  // PARTIAL tiles follow FULL ones in the lists
+  if (has_next) {
+    if (mnext) P::template load_k<true>(p, sb, s, h, ktn, gtid, off, kr);
+    else P::template load_k<false>(p, sb, s, h, ktn, gtid, off, kr);
+  }
+  f32x16 s0, s1;
+  s_product<T, D>(cur, qf, g, krow_a, s0, s1);
+  if (has_next) {
+    if (mnext) P::template load_v<true>(p, sb, s, h, ktn, gtid, off, vr, kid);
+    else P::template load_v<false>(p, sb, s, h, ktn, gtid, off, vr, kid);
+  }
+  softmax_update<T, D, MASKED>(s0, s1, st, cur, p, sb, kt, qi, qids, g);
+  if (has_next) P::store_k(nxt, gtid, kr);
+  pv_product<T, D>(cur, s0, s1, st, g, l32);
+  if (has_next) P::store_v(nxt, gtid, mnext, vr, kid);
+}
+
+// A workgroup owns 128 query rows of one (sequence, head) and walks the
+// row's kv-tile list.  With KG = 2 it has two groups of four waves over the
+// same query rows: group 0 takes list entries 0, 2, 4, ..., group 1 entries
+// 1, 3, 5, ..., each with its own double-buffered LDS stages, which halves
+// the serial chain of a long row.  At the end the two partial states
+// (running max, sum and accumulator) are combined through LDS:
+// m = max(m0, m1), l = l0 2^(m0-m) + l1 2^(m1-m), acc likewise.
+template <typename T, int D, bool PAGED, int KG>
+__global__ __launch_bounds__(kThreads * KG, 2) void prefill_kernel(FwdDev p) {
   using C = Cfg<T, D>;
   using P = Prefill<T, D, PAGED>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::kStage];
+  __shared__ __attribute__((aligned(16))) char smem[2 * KG * C::kStage];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = wave >> 2;             // kv group
+  const int gw = wave & 3;               // wave inside the group
+  const int gtid = tid & (kThreads - 1);  // thread inside the group
   const int l32 = lane & 31, g = lane >> 5;
+  char* gsm = smem + grp * 2 * C::kStage;
 
-  const uint32_t n_rows = (uint32_t)p.mask.n_seqs * p.n_qt;
-  const uint32_t w = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = (int)(w / n_rows);
-  const int row = p.row_order[w % n_rows];
+  // Dispatch order: row rank major (longest rows first, over all heads),
+  // head minor.  Workgroups go round-robin over the 8 XCDs, so head h always
+  // runs on XCD (h mod 8) when the head count is a multiple of 8 and its K/V
+  // stay in that XCD's L2.
+  const uint32_t w = blockIdx.x;
+  const int h = (int)(w % (uint32_t)p.num_heads);
+  const int row = p.row_order[w / (uint32_t)p.num_heads];
   const int s = row / p.n_qt, a = row % p.n_qt;
   const SeqBounds sb = seq_bounds(p.mask, s, p.max_lq, p.max_lk);
   if (a * kBM >= sb.lq) return;
@@ -439,7 +505,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(FwdDev p) {
   const int32_t* flist = p.full_idx + (int64_t)row * p.n_kt;
   const int32_t* plist = p.part_idx + (int64_t)row * p.n_kt;
 
-  const int qi = a * kBM + wave * 32 + l32;  // query row inside the sequence
+  const int qi = a * kBM + gw * 32 + l32;  // query row inside the sequence
   const bool qvalid = qi < sb.lq;
   const QIds qids = load_qids(p.mask, sb, qi);
 
@@ -478,66 +544,86 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(FwdDev p) {
   uint4 kr[C::kKChunks];
   uint4 vr[C::kKpt];
   KIds kid{0, 0};
-  const typename P::Offsets off = P::offsets(p, tid);
-  if (ntiles > 0) {
-    if (nfull > 0) {
-      P::template load_k<false>(p, sb, s, h, flist[0], tid, off, kr);
-      P::template load_v<false>(p, sb, s, h, flist[0], tid, off, vr, kid);
+  const typename P::Offsets off = P::offsets(p, gtid);
+  // The group's first tile is list entry grp.
+  if (grp < ntiles) {
+    if (grp < nfull) {
+      P::template load_k<false>(p, sb, s, h, flist[grp], gtid, off, kr);
+      P::template load_v<false>(p, sb, s, h, flist[grp], gtid, off, vr, kid);
     } else {
-      P::template load_k<true>(p, sb, s, h, plist[0], tid, off, kr);
-      P::template load_v<true>(p, sb, s, h, plist[0], tid, off, vr, kid);
+      P::template load_k<true>(p, sb, s, h, plist[grp - nfull], gtid, off, kr);
+      P::template load_v<true>(p, sb, s, h, plist[grp - nfull], gtid, off, vr, kid);
     }
-    P::store_k(smem, tid, kr);
-    P::store_v(smem, tid, nfull == 0, vr, kid);
+    P::store_k(gsm, gtid, kr);
+    P::store_v(gsm, gtid, grp >= nfull, vr, kid);
   }
   // Drain every outstanding load (the Q operand included) before the loops so
   // that no wait for them is carried into a loop body.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // Each iteration uses tile t from one LDS buffer and stages tile t+1 into
-  // the other: K(t+1) is loaded before the S product and stored after the
-  // softmax, V(t+1) is loaded after the S product and stored after the P V
-  // product, so at most one operand's staging registers are live at a time.
-  // FULL tiles: no mask code.
-  int t = 0;
-  for (; t < nfull; ++t) {
-    const bool has_next = t + 1 < ntiles;
-    const bool mnext = t + 1 >= nfull;
-    const int ktn = has_next ? (mnext ? plist[0] : flist[t + 1]) : 0;
-    char* cur = smem + (t & 1) * C::kStage;
-    char* nxt = smem + ((t + 1) & 1) * C::kStage;
-    if (has_next) {
-      if (mnext) P::template load_k<true>(p, sb, s, h, ktn, tid, off, kr);
-      else P::template load_k<false>(p, sb, s, h, ktn, tid, off, kr);
-    }
-    f32x16 s0, s1;
-    s_product<T, D>(cur, qf, g, krow_a, s0, s1);
-    if (has_next) {
-      if (mnext) P::template load_v<true>(p, sb, s, h, ktn, tid, off, vr, kid);
-      else P::template load_v<false>(p, sb, s, h, ktn, tid, off, vr, kid);
-    }
-    softmax_update<T, D, false>(s0, s1, st, cur, p, sb, flist[t], qi, qids, g);
-    if (has_next) P::store_k(nxt, tid, kr);
-    pv_product<T, D>(cur, s0, s1, st, g, l32);
-    if (has_next) P::store_v(nxt, tid, mnext, vr, kid);
+  // Iteration i handles list entry t = i*KG + grp of each group; all groups
+  // run the same number of iterations (one barrier each).
+  const int niter = (ntiles + KG - 1) / KG;
+  const int nfull_iter = nfull / KG;  // iterations whose tiles are FULL for every group
+  int i = 0;
+  for (; i < nfull_iter; ++i) {
+    const int t = i * KG + grp, tn = t + KG;
+    const bool has_next = tn < ntiles;
+    const bool mnext = tn >= nfull;
+    const int ktn = has_next ? (mnext ? plist[tn - nfull] : flist[tn]) : 0;
+    kv_step<T, D, PAGED, false>(gsm + (i & 1) * C::kStage, gsm + ((i + 1) & 1) * C::kStage,
+                                has_next, mnext, ktn, flist[t], p, sb, s, h, gtid, off, kr, vr, kid,
+                                qf, st, qi, qids, g, l32, krow_a);
     __syncthreads();
   }
-  // PARTIAL tiles: the element predicate, with the tile's key ids in LDS.
-  for (; t < ntiles; ++t) {
-    const bool has_next = t + 1 < ntiles;
-    const int ktn = has_next ? plist[t + 1 - nfull] : 0;
-    char* cur = smem + (t & 1) * C::kStage;
-    char* nxt = smem + ((t + 1) & 1) * C::kStage;
-    if (has_next) P::template load_k<true>(p, sb, s, h, ktn, tid, off, kr);
-    f32x16 s0, s1;
-    s_product<T, D>(cur, qf, g, krow_a, s0, s1);
-    if (has_next) P::template load_v<true>(p, sb, s, h, ktn, tid, off, vr, kid);
-    softmax_update<T, D, true>(s0, s1, st, cur, p, sb, plist[t - nfull], qi, qids, g);
-    if (has_next) P::store_k(nxt, tid, kr);
-    pv_product<T, D>(cur, s0, s1, st, g, l32);
-    if (has_next) P::store_v(nxt, tid, true, vr, kid);
+  for (; i < niter; ++i) {
+    const int t = i * KG + grp, tn = t + KG;
+    if (t < ntiles) {
+      const bool has_next = tn < ntiles;
+      const bool mnext = tn >= nfull;
+      const int ktn = has_next ? (mnext ? plist[tn - nfull] : flist[tn]) : 0;
+      const char* cur = gsm + (i & 1) * C::kStage;
+      char* nxt = gsm + ((i + 1) & 1) * C::kStage;
+      if (t < nfull) {
+        kv_step<T, D, PAGED, false>(cur, nxt, has_next, mnext, ktn, flist[t], p, sb, s, h, gtid,
+                                    off, kr, vr, kid, qf, st, qi, qids, g, l32, krow_a);
+      } else {
+        kv_step<T, D, PAGED, true>(cur, nxt, has_next, true, ktn, plist[t - nfull], p, sb, s, h,
+                                   gtid, off, kr, vr, kid, qf, st, qi, qids, g, l32, krow_a);
+      }
+    }
     __syncthreads();
+  }
+
+  if constexpr (KG == 2) {
+    // Group 1 hands its state to group 0 through LDS (lane-major, so the
+    // same lane of the partner wave holds the same query and d rows).
+    constexpr int kRegs = C::kDT * 16 + 2;
+    float* xch = reinterpret_cast<float*>(smem) + gw * kRegs * 64;
+    if (grp == 1) {
+#pragma unroll
+      for (int dt = 0; dt < C::kDT; ++dt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xch[(dt * 16 + r) * 64 + lane] = st.acc[dt][r];
+      }
+      xch[(kRegs - 2) * 64 + lane] = st.m;
+      xch[(kRegs - 1) * 64 + lane] = st.l;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xch[(kRegs - 2) * 64 + lane];
+    const float l1 = xch[(kRegs - 1) * 64 + lane];
+    const float m = fmaxf(st.m, m1);
+    const float mu = (m == -INFINITY) ? 0.f : m;
+    const float a0 = fast_exp2(st.m - mu), a1 = fast_exp2(m1 - mu);
+    st.l = st.l * a0 + l1 * a1;
+#pragma unroll
+    for (int dt = 0; dt < C::kDT; ++dt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc[dt][r] = st.acc[dt][r] * a0 + xch[(dt * 16 + r) * 64 + lane] * a1;
+    }
+    st.m = m;
   }
 
   // ---- epilogue: O = acc / l, LSE = m + ln(l) ------------------------------
@@ -566,15 +652,23 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(FwdDev p) {
   }
 }
 
+// Two kv groups where four LDS stages fit (every compiled type but fp32 with
+// head_dim 128, whose stage is twice as large).
+template <typename T, int D>
+constexpr int kv_groups() {
+  return 4 * Cfg<T, D>::kStage <= 160 * 1024 ? 2 : 1;
+}
+
 template <typename T, int D>
 hipError_t launch_typed(const FwdDev& p, bool paged, hipStream_t st) {
+  constexpr int KG = kv_groups<T, D>();
   const uint32_t n_rows = (uint32_t)p.mask.n_seqs * p.n_qt;
   const uint32_t grid = n_rows * (uint32_t)p.num_heads;
   if (grid == 0) return hipSuccess;
   if (paged) {
-    hipLaunchKernelGGL((prefill_kernel<T, D, true>), dim3(grid), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((prefill_kernel<T, D, true, KG>), dim3(grid), dim3(kThreads * KG), 0, st, p);
   } else {
-    hipLaunchKernelGGL((prefill_kernel<T, D, false>), dim3(grid), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((prefill_kernel<T, D, false, KG>), dim3(grid), dim3(kThreads * KG), 0, st, p);
   }
   return hipGetLastError();
 }
