@@ -140,6 +140,22 @@ def cpu_baseline(lay, q, k, v, kp, vp, bt, flops_total: float, budget_s: float =
             "sample": f"the whole workload x{passes} (float64 numpy), {dt:.1f} s"}
 
 
+def copy_calibration(mib: int, steps: int):
+    """A plain streaming kernel of known size: dst = src * 1 over fp32."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / max(steps, 1)
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
+                      "ms_per_copy": dt * 1e3, "steps": steps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -149,6 +165,10 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the workload, run a plain fp32 copy of MIB MiB (read once, "
+                         "written once) --steps times: the known-size kernel against which the "
+                         "HBM byte counters are scaled")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path; "
@@ -156,6 +176,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
     import synth
     from block_sparse_masked_amd import bmattn as bm
 
