@@ -22,7 +22,8 @@ LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libbmattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "mask_kernels.hip", "forward_prefill.hip", "forward_decode.hip"]
+SOURCES = ["api.hip", "mask_kernels.hip", "forward_prefill.hip", "forward_prefill_bf16.hip",
+           "forward_decode.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall",

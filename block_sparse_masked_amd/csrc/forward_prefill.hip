@@ -677,8 +677,7 @@ hipError_t launch_typed(const FwdDev& p, bool paged, hipStream_t st) {
 
 hipError_t launch_forward_prefill(const FwdDev& p, int dtype, bool paged, hipStream_t st) {
   if (p.block_m != kBM || p.block_n != kBN) return hipErrorInvalidValue;
-  if (dtype == BMATTN_BF16 && p.head_dim == 128) return launch_typed<__bf16, 128>(p, paged, st);
-  if (dtype == BMATTN_BF16 && p.head_dim == 64) return launch_typed<__bf16, 64>(p, paged, st);
+  if (dtype == BMATTN_BF16) return launch_forward_prefill_bf16(p, paged, st);
   if (dtype == BMATTN_F32 && p.head_dim == 128) return launch_typed<float, 128>(p, paged, st);
   if (dtype == BMATTN_F32 && p.head_dim == 64) return launch_typed<float, 64>(p, paged, st);
   return hipErrorInvalidValue;

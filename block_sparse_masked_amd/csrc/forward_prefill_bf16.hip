@@ -1,0 +1,557 @@
+// Block-sparse masked attention forward for bf16 inputs, query tiles of 128
+// rows (gfx950).
+//
+// Algorithm: Triton from First Principles, Ch. 21, section 21.1 -- the
+// online softmax over kv tiles with a running max m, a running sum l and an
+// accumulator rescaled by alpha = exp(m_old - m_new); section 21.2 -- the
+// element mask applied only where a tile straddles the mask boundary, and
+// tiles beyond it skipped.  Here the skip comes from the kv-tile lists of the
+// block mask: a workgroup walks its row's FULL tiles (no mask code) and then
+// its PARTIAL tiles (element predicate); EMPTY tiles are never loaded.
+//
+// Mapping onto CDNA4 (not the pages' design):
+//  * a kv group = 4 waves = the 128 query rows of one (sequence, head); each
+//    wave owns 32 query rows for the whole kv loop.  A workgroup holds two kv
+//    groups over the same rows that take alternate entries of the row's tile
+//    list and merge their states at the end;
+//  * K and V tiles (64 keys) go from HBM straight into LDS with
+//    global_load_lds_dwordx4 (no registers, no VALU): one wave instruction
+//    fills 1 KiB, each lane choosing which 16-byte piece of the tile lands in
+//    its slot.  Rows stay row-major with the 16-byte columns XOR-swizzled per
+//    row, so both operand reads below are free of bank conflicts;
+//  * a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows
+//    read with ds_read_b128, rows permuted by swapping bits 2 and 3 so each
+//    lane's 8 consecutive accumulator registers hold 8 consecutive keys; B =
+//    the wave's Q rows in registers), so lane l holds the scores of query
+//    (l % 32) and the row max / sum are lane-local plus one exchange with
+//    lane l ^ 32;
+//  * the probabilities feed acc^T += V^T P^T as the B operand straight from
+//    registers; the V^T operand comes from the row-major V tile through
+//    ds_read_b64_tr_b16, the gfx950 transposing LDS read: 16 lanes each read
+//    4 consecutive bf16 of one key row, and lane i receives column i of the
+//    resulting 4 x 16 block, i.e. 4 keys of one d;
+//  * the next tile's copies are issued before the current tile is used and
+//    waited for only at the end of the iteration, one barrier per tile;
+//  * exponentials are base 2 with log2(e) folded into the softmax scale, and
+//    the reference max moves only when it would grow by more than 8.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace bmattn {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+constexpr int kBM = 128;           // query rows of a workgroup
+constexpr int kBN = 64;            // keys of a kv tile
+constexpr int kGroupWaves = 4;     // waves of a kv group
+constexpr int kGroupThreads = 64 * kGroupWaves;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRescaleSlack = 8.0f;
+
+template <int D>
+struct Lay {
+  static constexpr int kRowB = D * 2;                 // bytes of one K/V row
+  static constexpr int kCh = kRowB / 16;               // 16-byte columns per row
+  static constexpr int kTileB = kBN * kRowB;           // bytes of a K (or V) tile
+  static constexpr int kV = kTileB;                    // V tile offset in a stage
+  static constexpr int kIds = 2 * kTileB;              // key ids of a PARTIAL tile
+  static constexpr int kStage = 2 * kTileB + 2 * kBN * 4;
+  static constexpr int kCopies = kTileB / 1024 / kGroupWaves;  // 1 KiB copies per wave per tile
+  static constexpr int kDT = D / 32;                   // 32-wide output d tiles
+  static_assert(kCopies >= 1 && kCopies * 1024 * kGroupWaves == kTileB, "tile / copy mismatch");
+};
+
+// Physical 16-byte column of logical column c in tile row r is c ^ swz(r).
+// D 128 (16 columns): the four low row bits with their halves swapped; D 64
+// (8 columns): row bits 1..3 rotated.  Either way the 16 rows read by 16
+// lanes of a K fragment, and the 4 rows x 64 bytes read by 32 lanes of a
+// transposing V read, cover 256 bytes of distinct banks.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Row index permutation of the 32-row MFMA operand: swaps bits 2 and 3.
+__device__ __forceinline__ int sigma(int i) {
+  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+// HBM -> LDS copies (global_load_lds_dword[x4]): lane i's 4 or 16 bytes from
+// `src` land at LDS byte lds + 4i or lds + 16i.  Written as inline assembly
+// so that the compiler does not treat the pending copies as writes that
+// every later LDS read might depend on (it would wait for them before the
+// first read of the current stage); the copies are waited for explicitly at
+// the end of each tile.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(const char, p)));
+}
+__device__ __forceinline__ void copy16(const void* src, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void copy4(const void* src, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+// Two floats -> two bf16 (round to nearest even) in one dword, lo first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
+
+// HBM -> LDS copies of one kv tile by one wave of a group.  Copy u of wave
+// gw fills 16-byte slots [64 (gw*kCopies + u), +64) of the tile; slot s holds
+// row s / kCh, physical column s % kCh, i.e. logical column
+// (s % kCh) ^ swz(row).  Rows past the sequence end read its last row: those
+// keys are hidden by the predicate (they only occur in PARTIAL tiles), and
+// the values read are finite.
+template <int D, bool PAGED>
+struct Copy {
+  using L = Lay<D>;
+  // Per-lane source row of each copy (sequence-relative key index, clamped).
+  static __device__ __forceinline__ void rows(const SeqBounds& sb, int kt, int gw, int lane,
+                                              int (&j)[L::kCopies], int (&col)[L::kCopies]) {
+#pragma unroll
+    for (int u = 0; u < L::kCopies; ++u) {
+      const int slot = (gw * L::kCopies + u) * 64 + lane;
+      const int r = slot / L::kCh;
+      col[u] = (slot % L::kCh) ^ swz<D>(r);
+      j[u] = max(min(kt * kBN + r, sb.lk - 1), 0);
+    }
+  }
+
+  // Pool rows of the copies' keys: contiguous K/V take sb.k0 + j; paged K/V
+  // go through the block table.
+  static __device__ __forceinline__ void pool_rows(const FwdDev& p, const SeqBounds& sb, int s,
+                                                   const int (&j)[L::kCopies],
+                                                   int64_t (&row)[L::kCopies]) {
+    if constexpr (!PAGED) {
+#pragma unroll
+      for (int u = 0; u < L::kCopies; ++u) row[u] = sb.k0 + j[u];
+    } else {
+      int32_t pe[L::kCopies];
+#pragma unroll
+      for (int u = 0; u < L::kCopies; ++u)
+        pe[u] = page_entry(p.block_table, p.bt_stride, s, j[u], p.page_size, p.page_shift);
+#pragma unroll
+      for (int u = 0; u < L::kCopies; ++u)
+        row[u] = row_in_page(pe[u], j[u], p.page_size, p.page_shift, p.num_pages);
+    }
+  }
+
+  static __device__ __forceinline__ void issue(const void* base, int64_t st, int64_t sh, int h,
+                                               const int64_t (&row)[L::kCopies],
+                                               const int (&col)[L::kCopies], char* tile, int gw) {
+#pragma unroll
+    for (int u = 0; u < L::kCopies; ++u) {
+      const char* src = static_cast<const char*>(base) + (row[u] * st + (int64_t)h * sh) * 2 + col[u] * 16;
+      copy16(src, lds_addr(tile + (gw * L::kCopies + u) * 1024));
+    }
+  }
+
+  // K and V of tile kt (and its key ids when it is PARTIAL) into `stage`.
+  static __device__ __forceinline__ void tile(const FwdDev& p, const SeqBounds& sb, int s, int h,
+                                              int kt, bool masked, int gw, int lane, char* stage) {
+    int j[L::kCopies], col[L::kCopies];
+    int64_t row[L::kCopies];
+    rows(sb, kt, gw, lane, j, col);
+    pool_rows(p, sb, s, j, row);
+    issue(p.k, p.k_st, p.k_sh, h, row, col, stage, gw);
+    issue(p.v, p.v_st, p.v_sh, h, row, col, stage + L::kV, gw);
+    if (masked && gw < 2) {
+      // wave 0: segment (shared-prefix) or role (strip-thinking) ids;
+      // wave 1: turn ids (strip-thinking).
+      const int32_t* ids = nullptr;
+      if (p.mask.kind == BMATTN_MASK_SHARED_PREFIX) ids = gw == 0 ? p.mask.seg_k : nullptr;
+      if (p.mask.kind == BMATTN_MASK_STRIP_THINKING) ids = gw == 0 ? p.mask.role_k : p.mask.turn_k;
+      if (ids != nullptr) {
+        const int jj = max(min(kt * kBN + lane, sb.lk - 1), 0);
+        copy4(ids + sb.k0 + jj, lds_addr(stage + L::kIds + gw * kBN * 4));
+      }
+    }
+  }
+};
+
+// Running state of the online softmax for the wave's 32 rows.
+template <int D>
+struct RowState {
+  f32x16 acc[D / 32];  // O^T accumulator: lane holds query (l % 32), 16 d rows per tile
+  float m, l;          // reference max (base-2 scaled) and this lane's partial sum
+};
+
+// Per-lane LDS byte offsets of the operand reads, fixed for the kernel.
+template <int D>
+struct Addr {
+  using L = Lay<D>;
+  int k[D / 16];          // K fragment of step ks, 32-key block 0 (block 1: + 32 rows)
+  int v[L::kDT][2];       // V^T transposing read of d tile dt, keys +0..3 / +4..7 (chunk 0)
+  __device__ __forceinline__ Addr(int lane) {
+    const int l32 = lane & 31, g = lane >> 5;
+    const int r = sigma(l32);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) k[ks] = r * L::kRowB + (((ks * 2 + g) ^ swz<D>(r)) << 4);
+    const int j = lane & 15, b = lane >> 4;
+#pragma unroll
+    for (int dt = 0; dt < L::kDT; ++dt) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int row = 8 * (b >> 1) + 4 * hf + (j >> 2);  // + 16 per key chunk
+        const int dcol = dt * 32 + 16 * (b & 1) + 4 * (j & 3);
+        v[dt][hf] = row * L::kRowB + (((dcol >> 3) ^ swz<D>(row)) << 4) + ((dcol * 2) & 15);
+      }
+    }
+  }
+};
+
+// S^T = K Q^T for the tile's two 32-key blocks.
+template <int D>
+__device__ __forceinline__ void s_product(const char* Ks, const bf16x8 (&q)[D / 16], const Addr<D>& ad,
+                                          f32x16& s0, f32x16& s1) {
+  using L = Lay<D>;
+  s0 = f32x16{};
+  s1 = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(Ks + ad.k[ks]);
+    const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(Ks + ad.k[ks] + 32 * L::kRowB);
+    s0 = mfma(k0, q[ks], s0);
+    s1 = mfma(k1, q[ks], s1);
+  }
+}
+
+// The element predicate on one tile's scores (lane layout of the S product):
+// hidden pairs become -inf.  Key ids of the tile come from LDS.
+template <int D, int KIND>
+__device__ __forceinline__ void mask_scores(float (&x)[32], const char* stage, const FwdDev& p,
+                                            const SeqBounds& sb, int kt, int qi, QIds qids, int g) {
+  const int32_t* ids = reinterpret_cast<const int32_t*>(stage + Lay<D>::kIds);
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int jj = b * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
+      KIds kid{0, 0};
+      if constexpr (KIND == BMATTN_MASK_SHARED_PREFIX || KIND == BMATTN_MASK_STRIP_THINKING)
+        kid = KIds{ids[jj], ids[kBN + jj]};
+      x[b * 16 + r] = visible_k<KIND>(p.mask, sb, qi, qids, kt * kBN + jj, kid) ? x[b * 16 + r]
+                                                                               : -INFINITY;
+    }
+  }
+}
+
+// The element mask (PARTIAL tiles), the online-softmax update and the
+// probabilities, written over the scores.
+// Register r of block b holds key kt*64 + b*32 + 16*(r/8) + 8*g + r%8.
+// Scores stay unscaled until the exponent: max(s * c) = c * max(s) for the
+// positive scale c, and exp2(s * c - m) is one fma and one exp.
+template <int D, bool MASKED>
+__device__ __forceinline__ void softmax_update(f32x16& s0, f32x16& s1, RowState<D>& st,
+                                               const char* stage, const FwdDev& p,
+                                               const SeqBounds& sb, int kt, int qi, QIds qids,
+                                               int g) {
+  if constexpr (MASKED) {
+    // The predicate is applied on a plain array copy: conditional element
+    // stores through a reference to the MFMA result vector were not kept by
+    // the compiler.  One straight-line instance per mask kind.
+    float x[32];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      x[r] = s0[r];
+      x[16 + r] = s1[r];
+    }
+    switch (p.mask.kind) {
+      case BMATTN_MASK_FULL: mask_scores<D, BMATTN_MASK_FULL>(x, stage, p, sb, kt, qi, qids, g); break;
+      case BMATTN_MASK_CAUSAL: mask_scores<D, BMATTN_MASK_CAUSAL>(x, stage, p, sb, kt, qi, qids, g); break;
+      case BMATTN_MASK_SHARED_PREFIX:
+        mask_scores<D, BMATTN_MASK_SHARED_PREFIX>(x, stage, p, sb, kt, qi, qids, g);
+        break;
+      default: mask_scores<D, BMATTN_MASK_STRIP_THINKING>(x, stage, p, sb, kt, qi, qids, g); break;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = x[r];
+      s1[r] = x[16 + r];
+    }
+  }
+  const float sl2 = p.scale_log2;
+  float mx = s0[0];
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+  // Lazy rescaling: the reference max st.m moves only when the tile's max
+  // exceeds it by more than kRescaleSlack (log2 units), or when it is still
+  // -inf.  exp2(s - m_ref) then stays below 2^kRescaleSlack, and O = acc / l
+  // is the same quantity for any reference, so skipping the rescale of acc
+  // changes only rounding.  The decision is per wave so acc is rescaled in a
+  // wave-uniform branch.
+  const bool grow = !(mx <= st.m + kRescaleSlack);
+  float m_ref = st.m;
+  if (__ballot(grow)) {
+    const float m_new = fmaxf(st.m, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(st.m - m_use);
+    st.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < Lay<D>::kDT; ++dt) st.acc[dt] *= alpha;
+    st.m = m_new;
+    m_ref = m_use;
+  }
+  // A row with nothing visible so far keeps -inf; its exponents use 0 so that
+  // masked scores give exp2(-inf) = 0, never -inf + inf.
+  if constexpr (MASKED) m_ref = (m_ref == -INFINITY) ? 0.f : m_ref;
+  float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s0[r] = fast_exp2(fmaf(s0[r], sl2, -m_ref));
+    s1[r] = fast_exp2(fmaf(s1[r], sl2, -m_ref));
+    r0 += s0[r];
+    r1 += s1[r];
+  }
+  st.l += r0 + r1;
+}
+
+// acc^T += V^T P^T.  P (B operand, 8 keys per lane) comes from the softmax
+// registers; V^T (A operand: d = lane % 32, keys 8*(lane/32) + 0..7 of each
+// 16-key chunk) from two transposing reads of the row-major V tile.
+template <int D>
+__device__ __forceinline__ void pv_product(const char* stage, const f32x16& p0, const f32x16& p1,
+                                           RowState<D>& st, const Addr<D>& ad) {
+  using L = Lay<D>;
+  const char* Vs = stage + L::kV;
+  bf16x8 pf[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f32x16& src = (k < 2) ? p0 : p1;
+    const int r0 = (k & 1) * 8;
+    uint4 u;
+    u.x = pack_bf16x2(src[r0 + 0], src[r0 + 1]);
+    u.y = pack_bf16x2(src[r0 + 2], src[r0 + 3]);
+    u.z = pack_bf16x2(src[r0 + 4], src[r0 + 5]);
+    u.w = pack_bf16x2(src[r0 + 6], src[r0 + 7]);
+    pf[k] = __builtin_bit_cast(bf16x8, u);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+#pragma unroll
+    for (int dt = 0; dt < L::kDT; ++dt) {
+      const char* base = Vs + k * 16 * L::kRowB;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, base + ad.v[dt][0]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, base + ad.v[dt][1]));
+      const i16x8 vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      st.acc[dt] = mfma(__builtin_bit_cast(bf16x8, vv), pf[k], st.acc[dt]);
+    }
+  }
+}
+
+// One kv tile for one wave: copies of the group's next tile into `nxt`,
+// then the S product, softmax and P V product of tile kt from `cur`.
+template <int D, bool PAGED, bool MASKED>
+__device__ __forceinline__ void kv_step(const char* cur, char* nxt, bool has_next, bool mnext,
+                                        int ktn, int kt, const FwdDev& p, const SeqBounds& sb,
+                                        int s, int h, int gw, int lane, const bf16x8 (&q)[D / 16],
+                                        const Addr<D>& ad, RowState<D>& st, int qi, QIds qids,
+                                        int g) {
+  if (has_next) Copy<D, PAGED>::tile(p, sb, s, h, ktn, MASKED || mnext, gw, lane, nxt);
+  f32x16 s0, s1;
+  s_product<D>(cur, q, ad, s0, s1);
+  softmax_update<D, MASKED>(s0, s1, st, cur, p, sb, kt, qi, qids, g);
+  pv_product<D>(cur, s0, s1, st, ad);
+}
+
+// Copies in flight are waited for by every wave, then the barrier makes all
+// waves' copies visible and frees the stage that was just read.
+__device__ __forceinline__ void end_of_tile() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// A workgroup owns 128 query rows of one (sequence, head) and walks the
+// row's kv-tile list.  With KG = 2 it has two kv groups over the same query
+// rows: group 0 takes list entries 0, 2, 4, ..., group 1 entries 1, 3, 5,
+// ..., each with its own double-buffered LDS stages.  At the end the two
+// partial states are combined through LDS: m = max(m0, m1),
+// l = l0 2^(m0-m) + l1 2^(m1-m), acc likewise.
+template <int D, bool PAGED, int KG>
+__global__ __launch_bounds__(kGroupThreads * KG, 1) void prefill_bf16_kernel(FwdDev p) {
+  using L = Lay<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * KG * L::kStage];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = wave / kGroupWaves;  // kv group
+  const int gw = wave % kGroupWaves;   // wave inside the group
+  const int l32 = lane & 31, g = lane >> 5;
+  char* gsm = smem + grp * 2 * L::kStage;
+
+  // Dispatch order: row rank major (longest rows first, over all heads),
+  // head minor.  Workgroups go round-robin over the 8 XCDs, so head h always
+  // runs on XCD (h mod 8) when the head count is a multiple of 8 and its K/V
+  // stay in that XCD's L2.
+  const uint32_t w = blockIdx.x;
+  const int h = (int)(w % (uint32_t)p.num_heads);
+  const int row = p.row_order[w / (uint32_t)p.num_heads];
+  const int s = row / p.n_qt, a = row % p.n_qt;
+  const SeqBounds sb = seq_bounds(p.mask, s, p.max_lq, p.max_lk);
+  if (a * kBM >= sb.lq) return;
+  const int nfull = p.full_cnt[row];
+  const int ntiles = nfull + p.part_cnt[row];
+  const int32_t* flist = p.full_idx + (int64_t)row * p.n_kt;
+  const int32_t* plist = p.part_idx + (int64_t)row * p.n_kt;
+
+  const int qi = a * kBM + gw * 32 + l32;  // query row inside the sequence
+  const bool qvalid = qi < sb.lq;
+  const QIds qids = load_qids(p.mask, sb, qi);
+
+  // Q operand (B of S^T = K Q^T), resident for the whole kv loop.
+  bf16x8 q[D / 16];
+  {
+    const char* qrow = static_cast<const char*>(p.q) +
+                       ((sb.q0 + (qvalid ? qi : 0)) * p.q_st + (int64_t)h * p.q_sh) * 2;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      uint4 x = qvalid ? *reinterpret_cast<const uint4*>(qrow + (ks * 16 + g * 8) * 2)
+                       : make_uint4(0, 0, 0, 0);
+      q[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  RowState<D> st;
+#pragma unroll
+  for (int dt = 0; dt < L::kDT; ++dt) st.acc[dt] = f32x16{};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  const Addr<D> ad(lane);
+
+  // The group's first tile is list entry grp.
+  if (grp < ntiles) {
+    const bool m0 = grp >= nfull;
+    Copy<D, PAGED>::tile(p, sb, s, h, m0 ? plist[grp - nfull] : flist[grp], m0, gw, lane, gsm);
+  }
+  end_of_tile();
+
+  // Iteration i handles list entry t = i*KG + grp of each group; all groups
+  // run the same number of iterations (one barrier each).
+  const int niter = (ntiles + KG - 1) / KG;
+  const int nfull_iter = nfull / KG;  // iterations whose tiles are FULL for every group
+  int i = 0;
+  for (; i < nfull_iter; ++i) {
+    const int t = i * KG + grp, tn = t + KG;
+    const bool has_next = tn < ntiles;
+    const bool mnext = tn >= nfull;
+    const int ktn = has_next ? (mnext ? plist[tn - nfull] : flist[tn]) : 0;
+    kv_step<D, PAGED, false>(gsm + (i & 1) * L::kStage, gsm + ((i + 1) & 1) * L::kStage, has_next,
+                             mnext, ktn, flist[t], p, sb, s, h, gw, lane, q, ad, st, qi, qids, g);
+    end_of_tile();
+  }
+  for (; i < niter; ++i) {
+    const int t = i * KG + grp, tn = t + KG;
+    if (t < ntiles) {
+      const bool has_next = tn < ntiles;
+      const bool mnext = tn >= nfull;
+      const int ktn = has_next ? (mnext ? plist[tn - nfull] : flist[tn]) : 0;
+      const char* cur = gsm + (i & 1) * L::kStage;
+      char* nxt = gsm + ((i + 1) & 1) * L::kStage;
+      if (t < nfull) {
+        kv_step<D, PAGED, false>(cur, nxt, has_next, mnext, ktn, flist[t], p, sb, s, h, gw, lane, q,
+                                 ad, st, qi, qids, g);
+      } else {
+        kv_step<D, PAGED, true>(cur, nxt, has_next, true, ktn, plist[t - nfull], p, sb, s, h, gw,
+                                lane, q, ad, st, qi, qids, g);
+      }
+    }
+    end_of_tile();
+  }
+
+  if constexpr (KG == 2) {
+    // Group 1 hands its state to group 0 through LDS (lane-major, so the
+    // same lane of the partner wave holds the same query and d rows).
+    constexpr int kRegs = L::kDT * 16 + 2;
+    float* xch = reinterpret_cast<float*>(smem) + gw * kRegs * 64;
+    if (grp == 1) {
+#pragma unroll
+      for (int dt = 0; dt < L::kDT; ++dt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xch[(dt * 16 + r) * 64 + lane] = st.acc[dt][r];
+      }
+      xch[(kRegs - 2) * 64 + lane] = st.m;
+      xch[(kRegs - 1) * 64 + lane] = st.l;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xch[(kRegs - 2) * 64 + lane];
+    const float l1 = xch[(kRegs - 1) * 64 + lane];
+    const float m = fmaxf(st.m, m1);
+    const float mu = (m == -INFINITY) ? 0.f : m;
+    const float a0 = fast_exp2(st.m - mu), a1 = fast_exp2(m1 - mu);
+    st.l = st.l * a0 + l1 * a1;
+#pragma unroll
+    for (int dt = 0; dt < L::kDT; ++dt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc[dt][r] = st.acc[dt][r] * a0 + xch[(dt * 16 + r) * 64 + lane] * a1;
+    }
+    st.m = m;
+  }
+
+  // ---- epilogue: O = acc / l, LSE = m + ln(l) ------------------------------
+  const float l_tot = st.l + __shfl_xor(st.l, 32);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qvalid) {
+    char* orow = static_cast<char*>(p.o) + ((sb.q0 + qi) * p.o_st + (int64_t)h * p.o_sh) * 2;
+#pragma unroll
+    for (int dt = 0; dt < L::kDT; ++dt) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d0 = dt * 32 + 8 * a4 + 4 * g;
+        const float o0 = st.acc[dt][a4 * 4 + 0] * inv, o1 = st.acc[dt][a4 * 4 + 1] * inv;
+        const float o2 = st.acc[dt][a4 * 4 + 2] * inv, o3 = st.acc[dt][a4 * 4 + 3] * inv;
+        *reinterpret_cast<uint2*>(orow + d0 * 2) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+      }
+    }
+    if (g == 0 && p.lse != nullptr) {
+      const float lse = l_tot > 0.f ? (st.m + __log2f(l_tot)) * kLn2 : -INFINITY;
+      p.lse[(int64_t)h * p.lse_sh + sb.q0 + qi] = lse;
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const FwdDev& p, bool paged, hipStream_t st) {
+  constexpr int KG = 2;
+  static_assert(2 * KG * Lay<D>::kStage <= 160 * 1024, "LDS stages exceed 160 KiB");
+  const uint32_t n_rows = (uint32_t)p.mask.n_seqs * p.n_qt;
+  const uint32_t grid = n_rows * (uint32_t)p.num_heads;
+  if (grid == 0) return hipSuccess;
+  if (paged) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true, KG>), dim3(grid), dim3(kGroupThreads * KG), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, false, KG>), dim3(grid), dim3(kGroupThreads * KG), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_forward_prefill_bf16(const FwdDev& p, bool paged, hipStream_t st) {
+  if (p.block_m != kBM || p.block_n != kBN) return hipErrorInvalidValue;
+  if (p.head_dim == 128) return launch_d<128>(p, paged, st);
+  if (p.head_dim == 64) return launch_d<64>(p, paged, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace bmattn

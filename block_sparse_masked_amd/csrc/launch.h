@@ -72,6 +72,7 @@ inline int32_t page_shift_of(int32_t page_size) {
 // Forward kernels.  Return hipErrorInvalidValue for a combination that is
 // not compiled (the caller checks support first).
 hipError_t launch_forward_prefill(const FwdDev& p, int dtype, bool paged, hipStream_t st);
+hipError_t launch_forward_prefill_bf16(const FwdDev& p, bool paged, hipStream_t st);
 hipError_t launch_forward_decode(const FwdDev& p, int dtype, bool paged, hipStream_t st);
 
 }  // namespace bmattn
