@@ -105,6 +105,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ void copy16(const void* src, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
+__device__ __forceinline__ void copy16s(uint32_t off, const void* base, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds) : "memory");
+}
 __device__ __forceinline__ void copy4(const void* src, uint32_t lds) {
   asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
@@ -123,9 +126,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 template <int D, bool PAGED>
 struct Copy {
   using L = Lay<D>;
-  // Per-lane source row of each copy (sequence-relative key index, clamped).
-  static __device__ __forceinline__ void rows(const SeqBounds& sb, int kt, int gw, int lane,
-                                              int (&j)[L::kCopies], int (&col)[L::kCopies]) {
+  uint32_t koff[L::kCopies], voff[L::kCopies];
+  bool short_ok;
+  __device__ __forceinline__ Copy(const FwdDev& p, int gw, int lane) {
+    short_ok = !PAGED && (int64_t)kBN * (p.k_st > p.v_st ? p.k_st : p.v_st) * 2 < (int64_t(1) << 31);
+#pragma unroll
+    for (int u = 0; u < L::kCopies; ++u) {
+      const int slot = (gw * L::kCopies + u) * 64 + lane;
+      const int r = slot / L::kCh, col = (slot % L::kCh) ^ swz<D>(r);
+      koff[u] = short_ok ? (uint32_t)(r * p.k_st * 2 + col * 16) : 0u;
+      voff[u] = short_ok ? (uint32_t)(r * p.v_st * 2 + col * 16) : 0u;
+    }
+  }
+  __device__ __forceinline__ void general(const FwdDev& p, const SeqBounds& sb, int s, int h, int kt,
+                                          int gw, int lane, char* stage) const {
+    int j[L::kCopies], col[L::kCopies];
+    int64_t row[L::kCopies];
 #pragma unroll
     for (int u = 0; u < L::kCopies; ++u) {
       const int slot = (gw * L::kCopies + u) * 64 + lane;
@@ -133,13 +149,6 @@ struct Copy {
       col[u] = (slot % L::kCh) ^ swz<D>(r);
       j[u] = max(min(kt * kBN + r, sb.lk - 1), 0);
     }
-  }
-
-  // Pool rows of the copies' keys: contiguous K/V take sb.k0 + j; paged K/V
-  // go through the block table.
-  static __device__ __forceinline__ void pool_rows(const FwdDev& p, const SeqBounds& sb, int s,
-                                                   const int (&j)[L::kCopies],
-                                                   int64_t (&row)[L::kCopies]) {
     if constexpr (!PAGED) {
 #pragma unroll
       for (int u = 0; u < L::kCopies; ++u) row[u] = sb.k0 + j[u];
@@ -152,30 +161,30 @@ struct Copy {
       for (int u = 0; u < L::kCopies; ++u)
         row[u] = row_in_page(pe[u], j[u], p.page_size, p.page_shift, p.num_pages);
     }
-  }
-
-  static __device__ __forceinline__ void issue(const void* base, int64_t st, int64_t sh, int h,
-                                               const int64_t (&row)[L::kCopies],
-                                               const int (&col)[L::kCopies], char* tile, int gw) {
 #pragma unroll
     for (int u = 0; u < L::kCopies; ++u) {
-      const char* src = static_cast<const char*>(base) + (row[u] * st + (int64_t)h * sh) * 2 + col[u] * 16;
-      copy16(src, lds_addr(tile + (gw * L::kCopies + u) * 1024));
+      const char* ks = static_cast<const char*>(p.k) + (row[u] * p.k_st + (int64_t)h * p.k_sh) * 2 + col[u] * 16;
+      copy16(ks, lds_addr(stage + (gw * L::kCopies + u) * 1024));
+    }
+#pragma unroll
+    for (int u = 0; u < L::kCopies; ++u) {
+      const char* vs = static_cast<const char*>(p.v) + (row[u] * p.v_st + (int64_t)h * p.v_sh) * 2 + col[u] * 16;
+      copy16(vs, lds_addr(stage + L::kV + (gw * L::kCopies + u) * 1024));
     }
   }
-
-  // K and V of tile kt (and its key ids when it is PARTIAL) into `stage`.
-  static __device__ __forceinline__ void tile(const FwdDev& p, const SeqBounds& sb, int s, int h,
-                                              int kt, bool masked, int gw, int lane, char* stage) {
-    int j[L::kCopies], col[L::kCopies];
-    int64_t row[L::kCopies];
-    rows(sb, kt, gw, lane, j, col);
-    pool_rows(p, sb, s, j, row);
-    issue(p.k, p.k_st, p.k_sh, h, row, col, stage, gw);
-    issue(p.v, p.v_st, p.v_sh, h, row, col, stage + L::kV, gw);
+  __device__ __forceinline__ void tile(const FwdDev& p, const SeqBounds& sb, int s, int h, int kt,
+                                       bool masked, int gw, int lane, char* stage) const {
+    if (short_ok && (kt + 1) * kBN <= sb.lk) {
+      const char* kb = static_cast<const char*>(p.k) + ((sb.k0 + (int64_t)kt * kBN) * p.k_st + (int64_t)h * p.k_sh) * 2;
+      const char* vb = static_cast<const char*>(p.v) + ((sb.k0 + (int64_t)kt * kBN) * p.v_st + (int64_t)h * p.v_sh) * 2;
+#pragma unroll
+      for (int u = 0; u < L::kCopies; ++u) copy16s(koff[u], kb, lds_addr(stage + (gw * L::kCopies + u) * 1024));
+#pragma unroll
+      for (int u = 0; u < L::kCopies; ++u) copy16s(voff[u], vb, lds_addr(stage + L::kV + (gw * L::kCopies + u) * 1024));
+    } else {
+      general(p, sb, s, h, kt, gw, lane, stage);
+    }
     if (masked && gw < 2) {
-      // wave 0: segment (shared-prefix) or role (strip-thinking) ids;
-      // wave 1: turn ids (strip-thinking).
       const int32_t* ids = nullptr;
       if (p.mask.kind == BMATTN_MASK_SHARED_PREFIX) ids = gw == 0 ? p.mask.seg_k : nullptr;
       if (p.mask.kind == BMATTN_MASK_STRIP_THINKING) ids = gw == 0 ? p.mask.role_k : p.mask.turn_k;
@@ -260,7 +269,7 @@ __device__ __forceinline__ void mask_scores(float (&x)[32], const char* stage, c
 // Scores stay unscaled until the exponent: max(s * c) = c * max(s) for the
 // positive scale c, and exp2(s * c - m) is one fma and one exp.
 template <int D, bool MASKED>
-__device__ __forceinline__ void softmax_update(f32x16& s0, f32x16& s1, RowState<D>& st,
+__device__ __forceinline__ void softmax_update(f32x16& s0, f32x16& s1, bf16x8 (&pf)[4], RowState<D>& st,
                                                const char* stage, const FwdDev& p,
                                                const SeqBounds& sb, int kt, int qi, QIds qids,
                                                int g) {
@@ -316,37 +325,33 @@ __device__ __forceinline__ void softmax_update(f32x16& s0, f32x16& s1, RowState<
   // A row with nothing visible so far keeps -inf; its exponents use 0 so that
   // masked scores give exp2(-inf) = 0, never -inf + inf.
   if constexpr (MASKED) m_ref = (m_ref == -INFINITY) ? 0.f : m_ref;
-  float r0 = 0.f, r1 = 0.f;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    s0[r] = fast_exp2(fmaf(s0[r], sl2, -m_ref));
-    s1[r] = fast_exp2(fmaf(s1[r], sl2, -m_ref));
-    r0 += s0[r];
-    r1 += s1[r];
+  for (int k = 0; k < 4; ++k) {
+    const f32x16& src = (k < 2) ? s0 : s1;
+    const int r0 = (k & 1) * 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = fast_exp2(fmaf(src[r0 + 2 * e], sl2, -m_ref));
+      const float b = fast_exp2(fmaf(src[r0 + 2 * e + 1], sl2, -m_ref));
+      w[e] = pack_bf16x2(a, b);
+      rs[k] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, rs[k], false);
+    }
+    pf[k] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
   }
-  st.l += r0 + r1;
+  st.l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 }
 
 // acc^T += V^T P^T.  P (B operand, 8 keys per lane) comes from the softmax
 // registers; V^T (A operand: d = lane % 32, keys 8*(lane/32) + 0..7 of each
 // 16-key chunk) from two transposing reads of the row-major V tile.
 template <int D>
-__device__ __forceinline__ void pv_product(const char* stage, const f32x16& p0, const f32x16& p1,
-                                           RowState<D>& st, const Addr<D>& ad) {
+__device__ __forceinline__ void pv_product(const char* stage, const bf16x8 (&pf)[4], RowState<D>& st,
+                                           const Addr<D>& ad) {
   using L = Lay<D>;
   const char* Vs = stage + L::kV;
-  bf16x8 pf[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const f32x16& src = (k < 2) ? p0 : p1;
-    const int r0 = (k & 1) * 8;
-    uint4 u;
-    u.x = pack_bf16x2(src[r0 + 0], src[r0 + 1]);
-    u.y = pack_bf16x2(src[r0 + 2], src[r0 + 3]);
-    u.z = pack_bf16x2(src[r0 + 4], src[r0 + 5]);
-    u.w = pack_bf16x2(src[r0 + 6], src[r0 + 7]);
-    pf[k] = __builtin_bit_cast(bf16x8, u);
-  }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
 #pragma unroll
@@ -366,13 +371,14 @@ template <int D, bool PAGED, bool MASKED>
 __device__ __forceinline__ void kv_step(const char* cur, char* nxt, bool has_next, bool mnext,
                                         int ktn, int kt, const FwdDev& p, const SeqBounds& sb,
                                         int s, int h, int gw, int lane, const bf16x8 (&q)[D / 16],
-                                        const Addr<D>& ad, RowState<D>& st, int qi, QIds qids,
-                                        int g) {
-  if (has_next) Copy<D, PAGED>::tile(p, sb, s, h, ktn, MASKED || mnext, gw, lane, nxt);
+                                        const Addr<D>& ad, const Copy<D, PAGED>& cp,
+                                        RowState<D>& st, int qi, QIds qids, int g) {
+  if (has_next) cp.tile(p, sb, s, h, ktn, MASKED || mnext, gw, lane, nxt);
   f32x16 s0, s1;
   s_product<D>(cur, q, ad, s0, s1);
-  softmax_update<D, MASKED>(s0, s1, st, cur, p, sb, kt, qi, qids, g);
-  pv_product<D>(cur, s0, s1, st, ad);
+  bf16x8 pf[4];
+  softmax_update<D, MASKED>(s0, s1, pf, st, cur, p, sb, kt, qi, qids, g);
+  pv_product<D>(cur, pf, st, ad);
 }
 
 // Copies in flight are waited for by every wave, then the barrier makes all
@@ -393,7 +399,8 @@ __global__ __launch_bounds__(kGroupThreads * KG, 1) void prefill_bf16_kernel(Fwd
   using L = Lay<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * KG * L::kStage];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave / kGroupWaves;  // kv group
   const int gw = wave % kGroupWaves;   // wave inside the group
   const int l32 = lane & 31, g = lane >> 5;
@@ -437,11 +444,12 @@ __global__ __launch_bounds__(kGroupThreads * KG, 1) void prefill_bf16_kernel(Fwd
   st.m = -INFINITY;
   st.l = 0.f;
   const Addr<D> ad(lane);
+  const Copy<D, PAGED> cp(p, gw, lane);
 
   // The group's first tile is list entry grp.
   if (grp < ntiles) {
     const bool m0 = grp >= nfull;
-    Copy<D, PAGED>::tile(p, sb, s, h, m0 ? plist[grp - nfull] : flist[grp], m0, gw, lane, gsm);
+    cp.tile(p, sb, s, h, m0 ? plist[grp - nfull] : flist[grp], m0, gw, lane, gsm);
   }
   end_of_tile();
 
@@ -456,7 +464,7 @@ __global__ __launch_bounds__(kGroupThreads * KG, 1) void prefill_bf16_kernel(Fwd
     const bool mnext = tn >= nfull;
     const int ktn = has_next ? (mnext ? plist[tn - nfull] : flist[tn]) : 0;
     kv_step<D, PAGED, false>(gsm + (i & 1) * L::kStage, gsm + ((i + 1) & 1) * L::kStage, has_next,
-                             mnext, ktn, flist[t], p, sb, s, h, gw, lane, q, ad, st, qi, qids, g);
+                             mnext, ktn, flist[t], p, sb, s, h, gw, lane, q, ad, cp, st, qi, qids, g);
     end_of_tile();
   }
   for (; i < niter; ++i) {
@@ -469,10 +477,10 @@ __global__ __launch_bounds__(kGroupThreads * KG, 1) void prefill_bf16_kernel(Fwd
       char* nxt = gsm + ((i + 1) & 1) * L::kStage;
       if (t < nfull) {
         kv_step<D, PAGED, false>(cur, nxt, has_next, mnext, ktn, flist[t], p, sb, s, h, gw, lane, q,
-                                 ad, st, qi, qids, g);
+                                 ad, cp, st, qi, qids, g);
       } else {
         kv_step<D, PAGED, true>(cur, nxt, has_next, true, ktn, plist[t - nfull], p, sb, s, h, gw,
-                                lane, q, ad, st, qi, qids, g);
+                                lane, q, ad, cp, st, qi, qids, g);
       }
     }
     end_of_tile();
