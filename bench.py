@@ -165,6 +165,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
+                    help="replay each step as a captured HIP graph (default) or launch it eagerly")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the workload, run a plain fp32 copy of MIB MiB (read once, "
                          "written once) --steps times: the known-size kernel against which the "
@@ -216,12 +218,39 @@ def main():
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    if args.launch == "graph":
+        # One step (mask build + forward) captured as a HIP graph on a side
+        # stream and replayed: the same kernels with the same arguments,
+        # without per-launch host work.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        # The forward kernel alone, timed with events on its launch stream.
+        for i in range(args.steps):
+            evs[i][0].record()
+            bm.forward(q, k, v, desc, tiles, block_table=bt, out=out, lse=lse, workspace=ws)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+    else:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     fwd_ms = [a.elapsed_time(b) for a, b in evs]
     fwd_avg_ms = sum(fwd_ms) / len(fwd_ms)
 
@@ -258,6 +287,7 @@ def main():
         "config": {"workload": args.workload, "seed": args.seed, "num_heads": H, "head_dim": D,
                    "seqlens_q": lay.seqlens_q if lay.n_seqs <= 16 else f"{lay.n_seqs} seqs",
                    "total_q": lay.total_q, "total_k": lay.total_k, "block_m": BM, "block_n": BN,
+                   "launch": args.launch,
                    "visible_pairs_per_head": pairs, "flops_per_step": flops},
         "roofline": roof,
         "detail": {"forward_kernel_ms": fwd_avg_ms, "forward_kernel_ms_min": min(fwd_ms),

@@ -243,24 +243,48 @@ __device__ __forceinline__ void s_product(const char* Ks, const bf16x8 (&q)[D / 
   }
 }
 
-// The element predicate on one tile's scores (lane layout of the S product):
-// hidden pairs become -inf.  Key ids of the tile come from LDS.
+// The element predicate on one tile, as a bit mask over the lane's 32
+// scores: bit 16 b + r is set when the key of register r of block b (key
+// kt*64 + 16 c + 8 g + e with c = 2 b + r / 8 and e = r % 8) is visible to
+// query qi.  The same predicate as visible_k(), evaluated per lane:
+//  * bounds and causality: the key must not pass lim = min(lk - 1,
+//    lk - lq + qi) (FULL: lk - 1).  Key offsets grow with the bit index, so
+//    the visible bits are a prefix whose length follows from lim directly;
+//  * shared-prefix and strip-thinking then AND in the key-id condition, the
+//    ids read from the tile's id stage 8 keys at a time.
 template <int D, int KIND>
-__device__ __forceinline__ void mask_scores(float (&x)[32], const char* stage, const FwdDev& p,
-                                            const SeqBounds& sb, int kt, int qi, QIds qids, int g) {
-  const int32_t* ids = reinterpret_cast<const int32_t*>(stage + Lay<D>::kIds);
+__device__ __forceinline__ uint32_t visible_bits(const char* kstage, const FwdDev& p,
+                                                 const SeqBounds& sb, int kt, int qi, QIds qids,
+                                                 int g) {
+  const int lim = (KIND == BMATTN_MASK_FULL) ? sb.lk - 1 : min(sb.lk - 1, sb.lk - sb.lq + qi);
+  const int n = lim - kt * kBN - 8 * g + 1;  // keys 16 c + e < n are visible
+  const int count = n <= 0 ? 0 : min(32, 8 * (n >> 4) + min(n & 15, 8));
+  uint32_t bits = qi < sb.lq ? (count >= 32 ? 0xffffffffu : ((1u << count) - 1u)) : 0u;
+  if constexpr (KIND == BMATTN_MASK_SHARED_PREFIX || KIND == BMATTN_MASK_STRIP_THINKING) {
+    const int32_t* ida = reinterpret_cast<const int32_t*>(kstage + Lay<D>::kIds);
+    const int32_t* idb = ida + kBN;
+    uint32_t keep = 0;
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
+    for (int c = 0; c < 4; ++c) {
+      const int j0 = 16 * c + 8 * g;
+      const int4 a0 = *reinterpret_cast<const int4*>(ida + j0);
+      const int4 a1 = *reinterpret_cast<const int4*>(ida + j0 + 4);
+      const int av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      if constexpr (KIND == BMATTN_MASK_SHARED_PREFIX) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int jj = b * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
-      KIds kid{0, 0};
-      if constexpr (KIND == BMATTN_MASK_SHARED_PREFIX || KIND == BMATTN_MASK_STRIP_THINKING)
-        kid = KIds{ids[jj], ids[kBN + jj]};
-      x[b * 16 + r] = visible_k<KIND>(p.mask, sb, qi, qids, kt * kBN + jj, kid) ? x[b * 16 + r]
-                                                                               : -INFINITY;
+        for (int e = 0; e < 8; ++e) keep |= (uint32_t)((av[e] == 0) | (av[e] == qids.seg)) << (8 * c + e);
+      } else {
+        const int4 b0 = *reinterpret_cast<const int4*>(idb + j0);
+        const int4 b1 = *reinterpret_cast<const int4*>(idb + j0 + 4);
+        const int bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          keep |= (uint32_t)!((av[e] == p.mask.think_role) & (bv[e] < qids.turn)) << (8 * c + e);
+      }
     }
+    bits &= keep;
   }
+  return bits;
 }
 
 // The element mask (PARTIAL tiles), the online-softmax update and the
@@ -274,27 +298,20 @@ __device__ __forceinline__ void softmax_update(f32x16& s0, f32x16& s1, bf16x8 (&
                                                const SeqBounds& sb, int kt, int qi, QIds qids,
                                                int g) {
   if constexpr (MASKED) {
-    // The predicate is applied on a plain array copy: conditional element
-    // stores through a reference to the MFMA result vector were not kept by
-    // the compiler.  One straight-line instance per mask kind.
-    float x[32];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      x[r] = s0[r];
-      x[16 + r] = s1[r];
-    }
+    uint32_t vis;
     switch (p.mask.kind) {
-      case BMATTN_MASK_FULL: mask_scores<D, BMATTN_MASK_FULL>(x, stage, p, sb, kt, qi, qids, g); break;
-      case BMATTN_MASK_CAUSAL: mask_scores<D, BMATTN_MASK_CAUSAL>(x, stage, p, sb, kt, qi, qids, g); break;
+      case BMATTN_MASK_FULL: vis = visible_bits<D, BMATTN_MASK_FULL>(stage, p, sb, kt, qi, qids, g); break;
+      case BMATTN_MASK_CAUSAL: vis = visible_bits<D, BMATTN_MASK_CAUSAL>(stage, p, sb, kt, qi, qids, g); break;
       case BMATTN_MASK_SHARED_PREFIX:
-        mask_scores<D, BMATTN_MASK_SHARED_PREFIX>(x, stage, p, sb, kt, qi, qids, g);
+        vis = visible_bits<D, BMATTN_MASK_SHARED_PREFIX>(stage, p, sb, kt, qi, qids, g);
         break;
-      default: mask_scores<D, BMATTN_MASK_STRIP_THINKING>(x, stage, p, sb, kt, qi, qids, g); break;
+      default: vis = visible_bits<D, BMATTN_MASK_STRIP_THINKING>(stage, p, sb, kt, qi, qids, g); break;
     }
+    // Every element is written, selected -- never a conditional store.
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s0[r] = x[r];
-      s1[r] = x[16 + r];
+      s0[r] = ((vis >> r) & 1u) ? s0[r] : -INFINITY;
+      s1[r] = ((vis >> (16 + r)) & 1u) ? s1[r] : -INFINITY;
     }
   }
   const float sl2 = p.scale_log2;
@@ -414,12 +431,19 @@ __global__ __launch_bounds__(kGroupThreads * KG, 1) void prefill_bf16_kernel(Fwd
   const int h = (int)(w % (uint32_t)p.num_heads);
   const int row = p.row_order[w / (uint32_t)p.num_heads];
   const int s = row / p.n_qt, a = row % p.n_qt;
-  const SeqBounds sb = seq_bounds(p.mask, s, p.max_lq, p.max_lk);
-  if (a * kBM >= sb.lq) return;
-  const int nfull = p.full_cnt[row];
-  const int ntiles = nfull + p.part_cnt[row];
+  // Everything that depends only on the row is loaded together with the
+  // sequence bounds (one round trip): the tile counts and the candidates for
+  // the group's first tile, list entry grp, which is FULL entry grp or
+  // PARTIAL entry grp - nfull (0 or 1).  Indices are clamped to the row.
   const int32_t* flist = p.full_idx + (int64_t)row * p.n_kt;
   const int32_t* plist = p.part_idx + (int64_t)row * p.n_kt;
+  const int nfull = p.full_cnt[row];
+  const int npart = p.part_cnt[row];
+  const int f_first = flist[min(grp, p.n_kt - 1)];
+  const int p_first0 = plist[0], p_first1 = plist[min(1, p.n_kt - 1)];
+  const SeqBounds sb = seq_bounds(p.mask, s, p.max_lq, p.max_lk);
+  if (a * kBM >= sb.lq) return;
+  const int ntiles = nfull + npart;
 
   const int qi = a * kBM + gw * 32 + l32;  // query row inside the sequence
   const bool qvalid = qi < sb.lq;
@@ -449,7 +473,7 @@ __global__ __launch_bounds__(kGroupThreads * KG, 1) void prefill_bf16_kernel(Fwd
   // The group's first tile is list entry grp.
   if (grp < ntiles) {
     const bool m0 = grp >= nfull;
-    cp.tile(p, sb, s, h, m0 ? plist[grp - nfull] : flist[grp], m0, gw, lane, gsm);
+    cp.tile(p, sb, s, h, m0 ? (grp - nfull == 0 ? p_first0 : p_first1) : f_first, m0, gw, lane, gsm);
   }
   end_of_tile();
 

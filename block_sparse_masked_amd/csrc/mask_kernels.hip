@@ -186,6 +186,66 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(TilesDev t, int rows
   if (r < rows) t.row_order[rank] = r;
 }
 
+// Small FULL / CAUSAL problems in one workgroup: classification needs no ids
+// there, so a wave classifies a whole row (64 kv tiles per step, the lists
+// compacted with ballots), and after one barrier the same workgroup ranks the
+// rows.  Same results as classify_kernel followed by schedule_kernel, in one
+// launch.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallMaxRows = 1024;
+
+__global__ __launch_bounds__(kSmallThreads) void classify_schedule_small_kernel(MaskDev m, TilesDev t,
+                                                                               int rows) {
+  __shared__ int32_t work[kSmallMaxRows];
+  __shared__ SeqBounds bounds[kSmallMaxRows];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int BM = t.block_m, BN = t.block_n;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // Every sequence's bounds first, all loads in flight at once (rows >=
+  // n_seqs, so the table fits).
+  for (int s = tid; s < t.n_seqs; s += kSmallThreads) bounds[s] = seq_bounds(m, s, t.max_lq, t.max_lk);
+  __syncthreads();
+  for (int row = wave; row < rows; row += kSmallThreads / 64) {
+    const int s = row / t.n_qt, a = row % t.n_qt;
+    const SeqBounds b = bounds[s];
+    const int qlo = a * BM;
+    const int64_t rowoff = (int64_t)row * t.n_kt;
+    int nf = 0, np = 0;
+    for (int c0 = 0; c0 < t.n_kt; c0 += 64) {
+      const int bidx = c0 + lane;
+      uint8_t cls = BMATTN_TILE_EMPTY;
+      if (bidx < t.n_kt) {
+        cls = classify_tile(m, b, qlo, bidx * BN, BM, BN, nullptr, 0, 0);
+        t.tile_class[rowoff + bidx] = cls;
+      }
+      const uint64_t fm = __ballot(cls == BMATTN_TILE_FULL);
+      const uint64_t pm = __ballot(cls == BMATTN_TILE_PARTIAL);
+      if (cls == BMATTN_TILE_FULL) t.full_idx[rowoff + nf + __popcll(fm & lt)] = bidx;
+      if (cls == BMATTN_TILE_PARTIAL) t.part_idx[rowoff + np + __popcll(pm & lt)] = bidx;
+      nf += __popcll(fm);
+      np += __popcll(pm);
+    }
+    for (int i = nf + lane; i < t.n_kt; i += 64) t.full_idx[rowoff + i] = -1;
+    for (int i = np + lane; i < t.n_kt; i += 64) t.part_idx[rowoff + i] = -1;
+    if (lane == 0) {
+      t.full_cnt[row] = nf;
+      t.part_cnt[row] = np;
+      work[row] = nf + np;
+    }
+  }
+  __syncthreads();
+  // Rank of row r: rows with more listed tiles, or as many and a lower index.
+  for (int r = tid; r < rows; r += kSmallThreads) {
+    const int my = work[r];
+    int rank = 0;
+    for (int k = 0; k < rows; ++k) {
+      const int w = work[k];
+      rank += (w > my) || (w == my && k < r);
+    }
+    t.row_order[rank] = r;
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void dense_mask_kernel(MaskDev m, TilesDev t, int seq,
                                                               uint8_t* out, int64_t stride) {
   const int64_t rows_out = (int64_t)t.n_qt * t.block_m;
@@ -273,6 +333,12 @@ __global__ __launch_bounds__(kThreads) void paged_gather_kernel(
 
 hipError_t launch_build_block_mask(const MaskDev& m, const TilesDev& t, hipStream_t st) {
   const int rows = t.n_seqs * t.n_qt;
+  const bool small = (m.kind == BMATTN_MASK_FULL || m.kind == BMATTN_MASK_CAUSAL) &&
+                     rows <= kSmallMaxRows && (int64_t)rows * t.n_kt <= 64 * 1024;
+  if (small) {
+    hipLaunchKernelGGL(classify_schedule_small_kernel, dim3(1), dim3(kSmallThreads), 0, st, m, t, rows);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(classify_kernel, dim3(rows), dim3(kThreads), 0, st, m, t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
