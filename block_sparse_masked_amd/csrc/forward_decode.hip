@@ -73,7 +73,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(FwdDev p) {
   constexpr int kCh = D * kElem / 16;  // lanes per key row
   constexpr int kEpc = 16 / kElem;     // elements per lane
   constexpr int kTpi = 64 / kCh;       // keys per wave load
-  constexpr int kSteps = kBN / kTpi;   // loads per tile
+  constexpr int kSteps = kBN / kTpi;   // loads per tile and operand
+  constexpr int kChunk = kSteps < 8 ? kSteps : 8;  // loads per operand in one chunk
+  constexpr int kChunks = kSteps / kChunk;         // chunks per tile
+  static_assert(kChunks * kChunk == kSteps, "chunking");
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane % kCh, tg = lane / kCh;
@@ -108,94 +111,118 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(FwdDev p) {
   const int64_t v_off = (int64_t)h * p.v_sh * kElem + c * 16;
   const int64_t k_rs = p.k_st * kElem, v_rs = p.v_st * kElem;
 
+  // The split's kv tiles: lane i holds the tile of list entry e0 + i.
+  const int my_e = e0 + lane;
+  const int my_kt = my_e < e1 ? (my_e < nfull ? flist[my_e] : plist[my_e - nfull]) : 0;
+  // Paged fast path: when a load's keys never straddle a page and the
+  // split's pages fit in one register per lane, every block-table entry the
+  // split needs is read once, up front; a load then picks its (wave-uniform)
+  // page with a lane read instead of a dependent global load.
+  const int ps = p.page_size;
+  const int ppt = ps < kBN ? kBN / ps : 1;  // pages per tile
+  const bool fast_pages = PAGED && ps % kTpi == 0 && (kBN % ps == 0 || ps % kBN == 0) &&
+                          ppt * p.split_tiles <= 64;
+  int32_t my_page = 0;
+  if (fast_pages) {
+    const int ti = lane / ppt, pi = lane % ppt;
+    const int kt_i = __shfl(my_kt, ti);
+    const int j = min(kt_i * kBN + pi * ps, sb.lk - 1);
+    if (e0 + ti < e1) my_page = page_entry(p.block_table, p.bt_stride, s, j, ps, p.page_shift);
+  }
+
   float acc[kEpc];
 #pragma unroll
   for (int e = 0; e < kEpc; ++e) acc[e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = p.scale_log2;
 
-  // Each tile is processed in sub-blocks of at most 16 loads per operand,
-  // which keeps the loads of one sub-block in flight together.
-  constexpr int kSub = kSteps < 16 ? kSteps : 16;
-  for (int e = e0; e < e1; ++e) {
-    const bool masked = e >= nfull;
-    const int kt = masked ? plist[e - nfull] : flist[e];
-    for (int sb0 = 0; sb0 < kSteps; sb0 += kSub) {
-      // All row lookups first (one wait for the block-table reads), then
-      // every K and V load of the sub-block in flight together.
-      int64_t rows[kSub];
-      if constexpr (PAGED) {
-        int32_t pe[kSub];
-#pragma unroll
-        for (int st = 0; st < kSub; ++st) {
-          const int j = min(kt * kBN + (sb0 + st) * kTpi + tg, sb.lk - 1);
-          pe[st] = page_entry(p.block_table, p.bt_stride, s, j, p.page_size, p.page_shift);
-        }
-#pragma unroll
-        for (int st = 0; st < kSub; ++st) {
-          const int j = kt * kBN + (sb0 + st) * kTpi + tg;
-          rows[st] = (!masked || j < sb.lk)
-                         ? row_in_page(pe[st], j, p.page_size, p.page_shift, p.num_pages)
-                         : -1;
-        }
-      } else {
-#pragma unroll
-        for (int st = 0; st < kSub; ++st) {
-          const int j = kt * kBN + (sb0 + st) * kTpi + tg;
-          rows[st] = (!masked || j < sb.lk) ? sb.k0 + j : -1;
-        }
+  // Pool row of the key that this lane's group reads at load step st of the
+  // split's tile ti (-1: past the sequence, read as zero).
+  auto key_row = [&](int ti, int st) -> int64_t {
+    const int kt = __shfl(my_kt, ti);
+    const int j = kt * kBN + st * kTpi + tg;
+    if (j >= sb.lk) return -1;
+    if constexpr (!PAGED) {
+      return sb.k0 + j;
+    } else {
+      if (fast_pages) {
+        const int slot = ps < kBN ? ti * ppt + (st * kTpi) / ps : ti;
+        const int32_t pe = __builtin_amdgcn_readlane(my_page, slot);
+        return row_in_page(pe, j, ps, p.page_shift, p.num_pages);
       }
-      uint4 kr[kSub];
-      uint4 vr[kSub];
+      return paged_row(p.block_table, p.bt_stride, s, j, ps, p.page_shift, p.num_pages);
+    }
+  };
+
+  // The split's loads stream in chunks of kChunk loads per operand: the next
+  // chunk's K and V loads are issued before the current chunk is used, so
+  // one chunk is always in flight.
+  const int nt = e1 - e0;
+  const int nchunks = nt * kChunks;
+  uint4 kr[2][kChunk], vr[2][kChunk];
+  auto issue = [&](int ci, uint4 (&kd)[kChunk], uint4 (&vd)[kChunk]) {
+    const int ti = ci / kChunks, st0 = (ci % kChunks) * kChunk;
+    int64_t rows[kChunk];
 #pragma unroll
-      for (int st = 0; st < kSub; ++st) {
-        kr[st] = rows[st] >= 0 ? *reinterpret_cast<const uint4*>(kbase + rows[st] * k_rs + k_off)
-                               : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < kChunk; ++u) rows[u] = key_row(ti, st0 + u);
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u)
+      kd[u] = rows[u] >= 0 ? *reinterpret_cast<const uint4*>(kbase + rows[u] * k_rs + k_off) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u)
+      vd[u] = rows[u] >= 0 ? *reinterpret_cast<const uint4*>(vbase + rows[u] * v_rs + v_off) : make_uint4(0, 0, 0, 0);
+  };
+  auto consume = [&](int ci, const uint4 (&kd)[kChunk], const uint4 (&vd)[kChunk]) {
+    const int ti = ci / kChunks, st0 = (ci % kChunks) * kChunk;
+    const bool masked = e0 + ti >= nfull;
+    float sc[kChunk];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      float kf[kEpc];
+      to_float<T>(kd[u], kf);
+      float d = 0.f;
+#pragma unroll
+      for (int i = 0; i < kEpc; ++i) d = fmaf(qv[i], kf[i], d);
+      sc[u] = group_sum<kCh>(d) * sl2;
+    }
+    if (masked) {
+      const int kt = __shfl(my_kt, ti);
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        const int j = kt * kBN + (st0 + u) * kTpi + tg;
+        if (!visible(p.mask, sb, a, qids, j)) sc[u] = -INFINITY;
       }
+    }
+    float mx = sc[0];
 #pragma unroll
-      for (int st = 0; st < kSub; ++st) {
-        vr[st] = rows[st] >= 0 ? *reinterpret_cast<const uint4*>(vbase + rows[st] * v_rs + v_off)
-                               : make_uint4(0, 0, 0, 0);
-      }
-      float sc[kSub];
+    for (int u = 1; u < kChunk; ++u) mx = fmaxf(mx, sc[u]);
 #pragma unroll
-      for (int st = 0; st < kSub; ++st) {
-        float kf[kEpc];
-        to_float<T>(kr[st], kf);
-        float d = 0.f;
+    for (int o = kCh; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float rs = 0.f;
 #pragma unroll
-        for (int i = 0; i < kEpc; ++i) d = fmaf(qv[i], kf[i], d);
-        sc[st] = group_sum<kCh>(d) * sl2;
-      }
-      if (masked) {
+    for (int i = 0; i < kEpc; ++i) acc[i] *= alpha;
 #pragma unroll
-        for (int st = 0; st < kSub; ++st) {
-          const int j = kt * kBN + (sb0 + st) * kTpi + tg;
-          if (!visible(p.mask, sb, a, qids, j)) sc[st] = -INFINITY;
-        }
-      }
-      float mx = sc[0];
+    for (int u = 0; u < kChunk; ++u) {
+      const float pr = fast_exp2(sc[u] - m_use);
+      rs += pr;
+      float vf[kEpc];
+      to_float<T>(vd[u], vf);
 #pragma unroll
-      for (int st = 1; st < kSub; ++st) mx = fmaxf(mx, sc[st]);
-#pragma unroll
-      for (int o = kCh; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float rs = 0.f;
-#pragma unroll
-      for (int i = 0; i < kEpc; ++i) acc[i] *= alpha;
-#pragma unroll
-      for (int st = 0; st < kSub; ++st) {
-        const float pr = fast_exp2(sc[st] - m_use);
-        rs += pr;
-        float vf[kEpc];
-        to_float<T>(vr[st], vf);
-#pragma unroll
-        for (int i = 0; i < kEpc; ++i) acc[i] = fmaf(pr, vf[i], acc[i]);
-      }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
+      for (int i = 0; i < kEpc; ++i) acc[i] = fmaf(pr, vf[i], acc[i]);
+    }
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+  };
+  issue(0, kr[0], vr[0]);
+  for (int ci = 0; ci < nchunks; ci += 2) {
+    if (ci + 1 < nchunks) issue(ci + 1, kr[1], vr[1]);
+    consume(ci, kr[0], vr[0]);
+    if (ci + 1 < nchunks) {
+      if (ci + 2 < nchunks) issue(ci + 2, kr[0], vr[0]);
+      consume(ci + 1, kr[1], vr[1]);
     }
   }
   // Combine the key groups of the wave (they share m_run).
