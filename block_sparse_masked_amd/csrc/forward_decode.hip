@@ -243,7 +243,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(FwdDev p) {
   }
 }
 
-// Merges the splits of each (row, head) in ascending split order.
+// Merges the splits of each (row, head): M = max_i m_i, f_i = 2^(m_i - M),
+// O = sum_i f_i acc_i / sum_i f_i l_i, the sums taken in ascending split
+// order (deterministic).  One wave per (row, head): lane i reads split i's
+// (m, l), and the accumulator loads of all splits are issued 8 at a time.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(FwdDev p) {
   constexpr int kPer = (D + 63) / 64;
@@ -259,21 +262,46 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(FwdDev p) {
   const int nsp = (ntot + p.split_tiles - 1) / p.split_tiles;
   const float* ws = p.ws + ((int64_t)row * p.n_splits * p.num_heads + h) * (D + 2);
   const int64_t sstride = (int64_t)p.num_heads * (D + 2);
-  float M = -INFINITY;
-  for (int i = 0; i < nsp; ++i) M = fmaxf(M, ws[i * sstride + D]);
-  const float Mu = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f;
+  float M = -INFINITY, L = 0.f;
   float o[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) o[k] = 0.f;
-  for (int i = 0; i < nsp; ++i) {
-    const float* w = ws + i * sstride;
-    const float f = fast_exp2(w[D] - Mu);
-    L += f * w[D + 1];
+  // Splits in batches of 64 (one per lane) for the weights.
+  float Mb = -INFINITY;
+  for (int b0 = 0; b0 < nsp; b0 += 64) {
+    const int i = b0 + lane;
+    const float mi = i < nsp ? ws[i * sstride + D] : -INFINITY;
+    Mb = fmaxf(Mb, mi);
+  }
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int d = lane + 64 * k;
-      if (d < D) o[k] += f * w[d];
+  for (int o2 = 32; o2 > 0; o2 >>= 1) Mb = fmaxf(Mb, __shfl_xor(Mb, o2));
+  M = Mb;
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  for (int b0 = 0; b0 < nsp; b0 += 64) {
+    const int i = b0 + lane;
+    const float f = i < nsp ? fast_exp2(ws[i * sstride + D] - Mu) : 0.f;
+    const float fl = i < nsp ? f * ws[i * sstride + D + 1] : 0.f;
+    // ascending-order sum of f_i l_i: prefix over lanes via readlane
+    const int nb = min(64, nsp - b0);
+    for (int j0 = 0; j0 < nb; j0 += 8) {
+      float x[8][kPer];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+          const int d = lane + 64 * k;
+          x[u][k] = (j0 + u < nb && d < D) ? ws[(b0 + j0 + u) * sstride + d] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + u < nb) {
+          const float fu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), j0 + u));
+          L += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fl), j0 + u));
+#pragma unroll
+          for (int k = 0; k < kPer; ++k) o[k] += fu * x[u][k];
+        }
+      }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
