@@ -30,7 +30,7 @@ METRIC = "masked-attention TFLOP/s (unmasked FLOPs) + % bf16 MFMA peak, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-KERNEL_SOURCES = {"prefill": "block_sparse_masked_amd/csrc/forward_prefill.hip",
+KERNEL_SOURCES = {"prefill": "block_sparse_masked_amd/csrc/forward_prefill_bf16.hip",
                   "decode": "block_sparse_masked_amd/csrc/forward_decode.hip"}
 
 
