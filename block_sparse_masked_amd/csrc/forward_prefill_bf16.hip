@@ -10,10 +10,9 @@
 // its PARTIAL tiles (element predicate); EMPTY tiles are never loaded.
 //
 // Mapping onto CDNA4 (not the pages' design):
-//  * a kv group = 4 waves = the 128 query rows of one (sequence, head); each
-//    wave owns 32 query rows for the whole kv loop.  A workgroup holds two kv
-//    groups over the same rows that take alternate entries of the row's tile
-//    list and merge their states at the end;
+//  * a workgroup = 4 waves = the 128 query rows of one (sequence, head);
+//    each wave owns 32 query rows for the whole kv loop.  Two workgroups
+//    share a CU and run out of phase;
 //  * K and V tiles (64 keys) go from HBM straight into LDS with
 //    global_load_lds_dwordx4 (no registers, no VALU): one wave instruction
 //    fills 1 KiB, each lane choosing which 16-byte piece of the tile lands in
@@ -30,8 +29,10 @@
 //    ds_read_b64_tr_b16, the gfx950 transposing LDS read: 16 lanes each read
 //    4 consecutive bf16 of one key row, and lane i receives column i of the
 //    resulting 4 x 16 block, i.e. 4 keys of one d;
-//  * the next tile's copies are issued before the current tile is used and
-//    waited for only at the end of the iteration, one barrier per tile;
+//  * the next tile's copies are issued one per 16-d step of the current
+//    tile's S product, between its MFMA pairs, and waited for only at the
+//    end of the iteration: one barrier per tile.  The list entry two tiles
+//    ahead is loaded early and read after that barrier;
 //  * exponentials are base 2 with log2(e) folded into the softmax scale, and
 //    the reference max moves only when it would grow by more than 8.
 #include <hip/hip_runtime.h>
@@ -53,8 +54,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 128;           // query rows of a workgroup
 constexpr int kBN = 64;            // keys of a kv tile
-constexpr int kGroupWaves = 4;     // waves of a kv group
-constexpr int kGroupThreads = 64 * kGroupWaves;
+constexpr int kWaves = 4;          // waves of a workgroup, 32 query rows each
+constexpr int kThreads = 64 * kWaves;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleSlack = 8.0f;
 
@@ -66,9 +67,9 @@ struct Lay {
   static constexpr int kV = kTileB;                    // V tile offset in a stage
   static constexpr int kIds = 2 * kTileB;              // key ids of a PARTIAL tile
   static constexpr int kStage = 2 * kTileB + 2 * kBN * 4;
-  static constexpr int kCopies = kTileB / 1024 / kGroupWaves;  // 1 KiB copies per wave per tile
+  static constexpr int kCopies = kTileB / 1024 / kWaves;  // 1 KiB copies per wave per tile
   static constexpr int kDT = D / 32;                   // 32-wide output d tiles
-  static_assert(kCopies >= 1 && kCopies * 1024 * kGroupWaves == kTileB, "tile / copy mismatch");
+  static_assert(kCopies >= 1 && kCopies * 1024 * kWaves == kTileB, "tile / copy mismatch");
 };
 
 // Physical 16-byte column of logical column c in tile row r is c ^ swz(r).
@@ -117,7 +118,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
-// HBM -> LDS copies of one kv tile by one wave of a group.  Copy u of wave
+// HBM -> LDS copies of one kv tile by one wave of the workgroup.  Copy u of wave
 // gw fills 16-byte slots [64 (gw*kCopies + u), +64) of the tile; slot s holds
 // row s / kCh, physical column s % kCh, i.e. logical column
 // (s % kCh) ^ swz(row).  Rows past the sequence end read its last row: those
@@ -170,6 +171,20 @@ struct Copy {
     for (int u = 0; u < L::kCopies; ++u) {
       const char* vs = static_cast<const char*>(p.v) + (row[u] * p.v_st + (int64_t)h * p.v_sh) * 2 + col[u] * 16;
       copy16(vs, lds_addr(stage + L::kV + (gw * L::kCopies + u) * 1024));
+    }
+  }
+  __device__ __forceinline__ bool whole(const SeqBounds& sb, int kt) const {
+    return short_ok && (kt + 1) * kBN <= sb.lk;
+  }
+  __device__ __forceinline__ void ids(const FwdDev& p, const SeqBounds& sb, int kt, int gw, int lane,
+                                      char* stage) const {
+    if (gw >= 2) return;
+    const int32_t* src = nullptr;
+    if (p.mask.kind == BMATTN_MASK_SHARED_PREFIX) src = gw == 0 ? p.mask.seg_k : nullptr;
+    if (p.mask.kind == BMATTN_MASK_STRIP_THINKING) src = gw == 0 ? p.mask.role_k : p.mask.turn_k;
+    if (src != nullptr) {
+      const int jj = max(min(kt * kBN + lane, sb.lk - 1), 0);
+      copy4(src + sb.k0 + jj, lds_addr(stage + L::kIds + gw * kBN * 4));
     }
   }
   __device__ __forceinline__ void tile(const FwdDev& p, const SeqBounds& sb, int s, int h, int kt,
@@ -227,19 +242,46 @@ struct Addr {
   }
 };
 
-// S^T = K Q^T for the tile's two 32-key blocks.
+// The wave's short-form copies of one whole kv tile: per-copy offsets,
+// the tile's K and V bases, and the LDS addresses of the wave's slots.
 template <int D>
+struct TileCopies {
+  uint32_t koff[Lay<D>::kCopies], voff[Lay<D>::kCopies];
+  const char* kb;
+  const char* vb;
+  uint32_t klds, vlds;  // LDS byte addresses of the wave's first K / V slot
+};
+// S^T = K Q^T for the tile's two 32-key blocks, K fragments read a few
+// steps ahead.  With COPIES, the wave's copies of the next (whole) tile are
+// issued one per 16-d step, after that step's two MFMAs: a copy that has to
+// wait for the memory pipeline then waits beside running matrix work.
+template <int D, bool COPIES>
 __device__ __forceinline__ void s_product(const char* Ks, const bf16x8 (&q)[D / 16], const Addr<D>& ad,
-                                          f32x16& s0, f32x16& s1) {
+                                          f32x16& s0, f32x16& s1, const TileCopies<D>& tc) {
   using L = Lay<D>;
+  constexpr int N = D / 16;
+  constexpr int kAhead = N < 4 ? N : 4;
+  static_assert(2 * L::kCopies == N, "one copy per 16-d step");
+  bf16x8 k0[N], k1[N];
   s0 = f32x16{};
   s1 = f32x16{};
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(Ks + ad.k[ks]);
-    const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(Ks + ad.k[ks] + 32 * L::kRowB);
-    s0 = mfma(k0, q[ks], s0);
-    s1 = mfma(k1, q[ks], s1);
+  for (int ks = 0; ks < kAhead; ++ks) {
+    k0[ks] = *reinterpret_cast<const bf16x8*>(Ks + ad.k[ks]);
+    k1[ks] = *reinterpret_cast<const bf16x8*>(Ks + ad.k[ks] + 32 * L::kRowB);
+  }
+#pragma unroll
+  for (int ks = 0; ks < N; ++ks) {
+    if (ks + kAhead < N) {
+      k0[ks + kAhead] = *reinterpret_cast<const bf16x8*>(Ks + ad.k[ks + kAhead]);
+      k1[ks + kAhead] = *reinterpret_cast<const bf16x8*>(Ks + ad.k[ks + kAhead] + 32 * L::kRowB);
+    }
+    s0 = mfma(k0[ks], q[ks], s0);
+    s1 = mfma(k1[ks], q[ks], s1);
+    if constexpr (COPIES) {
+      if (ks < L::kCopies) copy16s(tc.koff[ks], tc.kb, tc.klds + ks * 1024);
+      else copy16s(tc.voff[ks - L::kCopies], tc.vb, tc.vlds + (ks - L::kCopies) * 1024);
+    }
   }
 }
 
@@ -320,7 +362,15 @@ __device__ __forceinline__ void softmax_update(f32x16& s0, f32x16& s1, bf16x8 (&
   for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
 #pragma unroll
   for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+  {
+    // The partner half-wave's max without an LDS round trip: swapping the
+    // upper half of one copy with the lower half of another leaves
+    // {mx(l), mx(l ^ 32)} in the two results, in some order, on every lane.
+    const unsigned u = __float_as_uint(mx);
+    const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const unsigned lo = sw[0], hi = sw[1];  // elements copied out before any cast
+    mx = fmaxf(__uint_as_float(lo), __uint_as_float(hi)) * sl2;
+  }
   // Lazy rescaling: the reference max st.m moves only when the tile's max
   // exceeds it by more than kRescaleSlack (log2 units), or when it is still
   // -inf.  exp2(s - m_ref) then stays below 2^kRescaleSlack, and O = acc / l
@@ -382,20 +432,46 @@ __device__ __forceinline__ void pv_product(const char* stage, const bf16x8 (&pf)
   }
 }
 
-// One kv tile for one wave: copies of the group's next tile into `nxt`,
+// One kv tile for one wave: copies of the next tile into `nxt`,
 // then the S product, softmax and P V product of tile kt from `cur`.
 template <int D, bool PAGED, bool MASKED>
 __device__ __forceinline__ void kv_step(const char* cur, char* nxt, bool has_next, bool mnext,
-                                        int ktn, int kt, const FwdDev& p, const SeqBounds& sb,
+                                        int ktn, int kt, const int32_t* ahead, int& kt_ahead,
+                                        const FwdDev& p, const SeqBounds& sb,
                                         int s, int h, int gw, int lane, const bf16x8 (&q)[D / 16],
                                         const Addr<D>& ad, const Copy<D, PAGED>& cp,
                                         RowState<D>& st, int qi, QIds qids, int g) {
-  if (has_next) cp.tile(p, sb, s, h, ktn, MASKED || mnext, gw, lane, nxt);
+  using L = Lay<D>;
+  const bool whole = has_next && cp.whole(sb, ktn);
+  if (has_next && !whole) cp.tile(p, sb, s, h, ktn, MASKED || mnext, gw, lane, nxt);
+  if (whole && (MASKED || mnext)) cp.ids(p, sb, ktn, gw, lane, nxt);
+  // The list entry two tiles ahead, loaded now and used after the next
+  // barrier (whose wait covers it).
+  kt_ahead = ahead != nullptr ? *ahead : 0;
+  TileCopies<D> tc;
+#pragma unroll
+  for (int u = 0; u < L::kCopies; ++u) {
+    tc.koff[u] = cp.koff[u];
+    tc.voff[u] = cp.voff[u];
+  }
+  tc.kb = static_cast<const char*>(p.k) + ((sb.k0 + (int64_t)ktn * kBN) * p.k_st + (int64_t)h * p.k_sh) * 2;
+  tc.vb = static_cast<const char*>(p.v) + ((sb.k0 + (int64_t)ktn * kBN) * p.v_st + (int64_t)h * p.v_sh) * 2;
+  tc.klds = lds_addr(nxt + gw * L::kCopies * 1024);
+  tc.vlds = lds_addr(nxt + L::kV + gw * L::kCopies * 1024);
   f32x16 s0, s1;
-  s_product<D>(cur, q, ad, s0, s1);
+  if (whole) s_product<D, true>(cur, q, ad, s0, s1, tc);
+  else s_product<D, false>(cur, q, ad, s0, s1, tc);
   bf16x8 pf[4];
   softmax_update<D, MASKED>(s0, s1, pf, st, cur, p, sb, kt, qi, qids, g);
   pv_product<D>(cur, pf, st, ad);
+}
+
+// A loaded value kept in its vector register until this point (after the
+// end-of-tile wait), then taken as wave-uniform: its load is never waited
+// for separately, which would also wait for the copies issued before it.
+__device__ __forceinline__ int uniform_after_wait(int v) {
+  asm volatile("" : "+v"(v));
+  return __builtin_amdgcn_readfirstlane(v);
 }
 
 // Copies in flight are waited for by every wave, then the barrier makes all
@@ -405,23 +481,18 @@ __device__ __forceinline__ void end_of_tile() {
   __syncthreads();
 }
 
-// A workgroup owns 128 query rows of one (sequence, head) and walks the
-// row's kv-tile list.  With KG = 2 it has two kv groups over the same query
-// rows: group 0 takes list entries 0, 2, 4, ..., group 1 entries 1, 3, 5,
-// ..., each with its own double-buffered LDS stages.  At the end the two
-// partial states are combined through LDS: m = max(m0, m1),
-// l = l0 2^(m0-m) + l1 2^(m1-m), acc likewise.
-template <int D, bool PAGED, int KG>
-__global__ __launch_bounds__(kGroupThreads * KG, 1) void prefill_bf16_kernel(FwdDev p) {
+// A workgroup (four waves) owns 128 query rows of one (sequence, head) and
+// walks the row's kv-tile list with a double-buffered LDS stage.  Two
+// workgroups share a CU (66 KiB of LDS each) and synchronise independently,
+// so one workgroup's softmax runs beside the other's matrix work.
+template <int D, bool PAGED>
+__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(FwdDev p) {
   using L = Lay<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * KG * L::kStage];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * L::kStage];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave / kGroupWaves;  // kv group
-  const int gw = wave % kGroupWaves;   // wave inside the group
   const int l32 = lane & 31, g = lane >> 5;
-  char* gsm = smem + grp * 2 * L::kStage;
 
   // Dispatch order: row rank major (longest rows first, over all heads),
   // head minor.  Workgroups go round-robin over the 8 XCDs, so head h always
@@ -433,19 +504,19 @@ __global__ __launch_bounds__(kGroupThreads * KG, 1) void prefill_bf16_kernel(Fwd
   const int s = row / p.n_qt, a = row % p.n_qt;
   // Everything that depends only on the row is loaded together with the
   // sequence bounds (one round trip): the tile counts and the candidates for
-  // the group's first tile, list entry grp, which is FULL entry grp or
-  // PARTIAL entry grp - nfull (0 or 1).  Indices are clamped to the row.
+  // the first tile, FULL entry 0 or PARTIAL entry 0.  Indices are clamped to
+  // the row.
   const int32_t* flist = p.full_idx + (int64_t)row * p.n_kt;
   const int32_t* plist = p.part_idx + (int64_t)row * p.n_kt;
   const int nfull = p.full_cnt[row];
   const int npart = p.part_cnt[row];
-  const int f_first = flist[min(grp, p.n_kt - 1)];
-  const int p_first0 = plist[0], p_first1 = plist[min(1, p.n_kt - 1)];
+  const int f_first = flist[0];
+  const int p_first = plist[0];
   const SeqBounds sb = seq_bounds(p.mask, s, p.max_lq, p.max_lk);
   if (a * kBM >= sb.lq) return;
   const int ntiles = nfull + npart;
 
-  const int qi = a * kBM + gw * 32 + l32;  // query row inside the sequence
+  const int qi = a * kBM + wave * 32 + l32;  // query row inside the sequence
   const bool qvalid = qi < sb.lq;
   const QIds qids = load_qids(p.mask, sb, qi);
 
@@ -468,76 +539,44 @@ __global__ __launch_bounds__(kGroupThreads * KG, 1) void prefill_bf16_kernel(Fwd
   st.m = -INFINITY;
   st.l = 0.f;
   const Addr<D> ad(lane);
-  const Copy<D, PAGED> cp(p, gw, lane);
+  const Copy<D, PAGED> cp(p, wave, lane);
 
-  // The group's first tile is list entry grp.
-  if (grp < ntiles) {
-    const bool m0 = grp >= nfull;
-    cp.tile(p, sb, s, h, m0 ? (grp - nfull == 0 ? p_first0 : p_first1) : f_first, m0, gw, lane, gsm);
+  // List entry t (FULL entries first, then PARTIAL ones), or none.
+  auto entry_ptr = [&](int t) -> const int32_t* {
+    return t < ntiles ? (t < nfull ? flist + t : plist + (t - nfull)) : nullptr;
+  };
+  // The first tile's copies, then the entry of the second tile behind them.
+  int kt_cur = 0, kt_nxt = 0;
+  if (ntiles > 0) {
+    const bool m0 = nfull == 0;
+    kt_cur = m0 ? p_first : f_first;
+    cp.tile(p, sb, s, h, kt_cur, m0, wave, lane, smem);
+    if (ntiles > 1) kt_nxt = *entry_ptr(1);
   }
   end_of_tile();
 
-  // Iteration i handles list entry t = i*KG + grp of each group; all groups
-  // run the same number of iterations (one barrier each).
-  const int niter = (ntiles + KG - 1) / KG;
-  const int nfull_iter = nfull / KG;  // iterations whose tiles are FULL for every group
-  int i = 0;
-  for (; i < nfull_iter; ++i) {
-    const int t = i * KG + grp, tn = t + KG;
-    const bool has_next = tn < ntiles;
-    const bool mnext = tn >= nfull;
-    const int ktn = has_next ? (mnext ? plist[tn - nfull] : flist[tn]) : 0;
-    kv_step<D, PAGED, false>(gsm + (i & 1) * L::kStage, gsm + ((i + 1) & 1) * L::kStage, has_next,
-                             mnext, ktn, flist[t], p, sb, s, h, gw, lane, q, ad, cp, st, qi, qids, g);
+  // Iteration t handles list entry t: FULL tiles first (no mask code), then
+  // the PARTIAL ones.  One barrier per tile.
+  int t = 0;
+  for (; t < nfull; ++t) {
+    const bool has_next = t + 1 < ntiles;
+    const bool mnext = t + 1 >= nfull;
+    int kt_ahead;
+    kv_step<D, PAGED, false>(smem + (t & 1) * L::kStage, smem + ((t + 1) & 1) * L::kStage, has_next,
+                             mnext, kt_nxt, kt_cur, entry_ptr(t + 2), kt_ahead, p, sb, s, h, wave,
+                             lane, q, ad, cp, st, qi, qids, g);
     end_of_tile();
+    kt_cur = kt_nxt;
+    kt_nxt = uniform_after_wait(kt_ahead);
   }
-  for (; i < niter; ++i) {
-    const int t = i * KG + grp, tn = t + KG;
-    if (t < ntiles) {
-      const bool has_next = tn < ntiles;
-      const bool mnext = tn >= nfull;
-      const int ktn = has_next ? (mnext ? plist[tn - nfull] : flist[tn]) : 0;
-      const char* cur = gsm + (i & 1) * L::kStage;
-      char* nxt = gsm + ((i + 1) & 1) * L::kStage;
-      if (t < nfull) {
-        kv_step<D, PAGED, false>(cur, nxt, has_next, mnext, ktn, flist[t], p, sb, s, h, gw, lane, q,
-                                 ad, cp, st, qi, qids, g);
-      } else {
-        kv_step<D, PAGED, true>(cur, nxt, has_next, true, ktn, plist[t - nfull], p, sb, s, h, gw,
-                                lane, q, ad, cp, st, qi, qids, g);
-      }
-    }
+  for (; t < ntiles; ++t) {
+    int kt_ahead;
+    kv_step<D, PAGED, true>(smem + (t & 1) * L::kStage, smem + ((t + 1) & 1) * L::kStage,
+                            t + 1 < ntiles, true, kt_nxt, kt_cur, entry_ptr(t + 2), kt_ahead, p, sb,
+                            s, h, wave, lane, q, ad, cp, st, qi, qids, g);
     end_of_tile();
-  }
-
-  if constexpr (KG == 2) {
-    // Group 1 hands its state to group 0 through LDS (lane-major, so the
-    // same lane of the partner wave holds the same query and d rows).
-    constexpr int kRegs = L::kDT * 16 + 2;
-    float* xch = reinterpret_cast<float*>(smem) + gw * kRegs * 64;
-    if (grp == 1) {
-#pragma unroll
-      for (int dt = 0; dt < L::kDT; ++dt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) xch[(dt * 16 + r) * 64 + lane] = st.acc[dt][r];
-      }
-      xch[(kRegs - 2) * 64 + lane] = st.m;
-      xch[(kRegs - 1) * 64 + lane] = st.l;
-    }
-    __syncthreads();
-    if (grp == 1) return;
-    const float m1 = xch[(kRegs - 2) * 64 + lane];
-    const float l1 = xch[(kRegs - 1) * 64 + lane];
-    const float m = fmaxf(st.m, m1);
-    const float mu = (m == -INFINITY) ? 0.f : m;
-    const float a0 = fast_exp2(st.m - mu), a1 = fast_exp2(m1 - mu);
-    st.l = st.l * a0 + l1 * a1;
-#pragma unroll
-    for (int dt = 0; dt < L::kDT; ++dt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.acc[dt][r] = st.acc[dt][r] * a0 + xch[(dt * 16 + r) * 64 + lane] * a1;
-    }
-    st.m = m;
+    kt_cur = kt_nxt;
+    kt_nxt = uniform_after_wait(kt_ahead);
   }
 
   // ---- epilogue: O = acc / l, LSE = m + ln(l) ------------------------------
@@ -564,15 +603,14 @@ __global__ __launch_bounds__(kGroupThreads * KG, 1) void prefill_bf16_kernel(Fwd
 
 template <int D>
 hipError_t launch_d(const FwdDev& p, bool paged, hipStream_t st) {
-  constexpr int KG = 2;
-  static_assert(2 * KG * Lay<D>::kStage <= 160 * 1024, "LDS stages exceed 160 KiB");
+  static_assert(2 * 2 * Lay<D>::kStage <= 160 * 1024, "two workgroups' LDS stages exceed 160 KiB");
   const uint32_t n_rows = (uint32_t)p.mask.n_seqs * p.n_qt;
   const uint32_t grid = n_rows * (uint32_t)p.num_heads;
   if (grid == 0) return hipSuccess;
   if (paged) {
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, true, KG>), dim3(grid), dim3(kGroupThreads * KG), 0, st, p);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), dim3(grid), dim3(kThreads), 0, st, p);
   } else {
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, false, KG>), dim3(grid), dim3(kGroupThreads * KG), 0, st, p);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, false>), dim3(grid), dim3(kThreads), 0, st, p);
   }
   return hipGetLastError();
 }
