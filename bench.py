@@ -218,10 +218,14 @@ def main():
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
+    graph_steps = 1
     if args.launch == "graph":
-        # One step (mask build + forward) captured as a HIP graph on a side
-        # stream and replayed: the same kernels with the same arguments,
-        # without per-launch host work.
+        # G consecutive steps (mask build + forward each) captured as one HIP
+        # graph on a side stream and replayed K / G times: the same kernels
+        # with the same arguments, without per-launch host work, and one
+        # graph launch per G steps.  G is the largest divisor of K up to 20,
+        # so exactly K steps are timed.
+        graph_steps = max(d for d in range(1, 21) if args.steps % d == 0)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -229,12 +233,13 @@ def main():
         torch.cuda.current_stream().wait_stream(side)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            step()
-        for _ in range(args.warmup):
+            for _ in range(graph_steps):
+                step()
+        for _ in range(max(1, args.warmup // graph_steps)):
             graph.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(args.steps // graph_steps):
             graph.replay()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -287,7 +292,7 @@ def main():
         "config": {"workload": args.workload, "seed": args.seed, "num_heads": H, "head_dim": D,
                    "seqlens_q": lay.seqlens_q if lay.n_seqs <= 16 else f"{lay.n_seqs} seqs",
                    "total_q": lay.total_q, "total_k": lay.total_k, "block_m": BM, "block_n": BN,
-                   "launch": args.launch,
+                   "launch": args.launch, "graph_steps": graph_steps,
                    "visible_pairs_per_head": pairs, "flops_per_step": flops},
         "roofline": roof,
         "detail": {"forward_kernel_ms": fwd_avg_ms, "forward_kernel_ms_min": min(fwd_ms),

@@ -8,6 +8,8 @@
 // every empty tile on a scalar read, as in Ch. 9, section 9.2.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -186,64 +188,77 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(TilesDev t, int rows
   if (r < rows) t.row_order[rank] = r;
 }
 
-// Small FULL / CAUSAL problems in one workgroup: classification needs no ids
-// there, so a wave classifies a whole row (64 kv tiles per step, the lists
-// compacted with ballots), and after one barrier the same workgroup ranks the
-// rows.  Same results as classify_kernel followed by schedule_kernel, in one
+// Small FULL / CAUSAL problems in one workgroup.  Without ids, a row's
+// classes follow from the sequence bounds in closed form: the non-empty kv
+// tiles are j < ne, with ne = floor(kmax / BN) + 1 for the last visible key
+// kmax = min(lk - 1, off + qhi - 1) (CAUSAL; FULL: lk - 1), and of those the
+// FULL ones are the prefix j < nf, nf = floor((lim + 1) / BN) for
+// lim = min(lk - 1, off + qlo) (CAUSAL; FULL: lk - 1) when the row's queries
+// lie inside the sequence (else nf = 0); the rest are PARTIAL.  This is the
+// tile classification of classify_tile() restricted to these two kinds.  So
+// the workgroup counts every row, writes the classes and both lists in one
+// flat coalesced pass, and ranks the rows with several threads per row.
+// Same results as classify_kernel followed by schedule_kernel, in one
 // launch.
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallMaxRows = 1024;
 
 __global__ __launch_bounds__(kSmallThreads) void classify_schedule_small_kernel(MaskDev m, TilesDev t,
                                                                                int rows) {
-  __shared__ int32_t work[kSmallMaxRows];
   __shared__ SeqBounds bounds[kSmallMaxRows];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int BM = t.block_m, BN = t.block_n;
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  // Every sequence's bounds first, all loads in flight at once (rows >=
-  // n_seqs, so the table fits).
+  __shared__ int32_t nf_s[kSmallMaxRows], np_s[kSmallMaxRows], rank_s[kSmallMaxRows];
+  const int tid = threadIdx.x;
+  const int BM = t.block_m, BN = t.block_n, nkt = t.n_kt;
+  const bool causal = m.kind == BMATTN_MASK_CAUSAL;
+  // Sequence bounds (rows >= n_seqs, so the table fits).
   for (int s = tid; s < t.n_seqs; s += kSmallThreads) bounds[s] = seq_bounds(m, s, t.max_lq, t.max_lk);
+  for (int r = tid; r < rows; r += kSmallThreads) rank_s[r] = 0;
   __syncthreads();
-  for (int row = wave; row < rows; row += kSmallThreads / 64) {
-    const int s = row / t.n_qt, a = row % t.n_qt;
-    const SeqBounds b = bounds[s];
-    const int qlo = a * BM;
-    const int64_t rowoff = (int64_t)row * t.n_kt;
-    int nf = 0, np = 0;
-    for (int c0 = 0; c0 < t.n_kt; c0 += 64) {
-      const int bidx = c0 + lane;
-      uint8_t cls = BMATTN_TILE_EMPTY;
-      if (bidx < t.n_kt) {
-        cls = classify_tile(m, b, qlo, bidx * BN, BM, BN, nullptr, 0, 0);
-        t.tile_class[rowoff + bidx] = cls;
-      }
-      const uint64_t fm = __ballot(cls == BMATTN_TILE_FULL);
-      const uint64_t pm = __ballot(cls == BMATTN_TILE_PARTIAL);
-      if (cls == BMATTN_TILE_FULL) t.full_idx[rowoff + nf + __popcll(fm & lt)] = bidx;
-      if (cls == BMATTN_TILE_PARTIAL) t.part_idx[rowoff + np + __popcll(pm & lt)] = bidx;
-      nf += __popcll(fm);
-      np += __popcll(pm);
+  // Per-row counts.
+  for (int row = tid; row < rows; row += kSmallThreads) {
+    const SeqBounds b = bounds[row / t.n_qt];
+    const int64_t qlo = (int64_t)(row % t.n_qt) * BM;
+    int nf = 0, ne = 0;
+    if (qlo < b.lq && b.lk > 0) {
+      const int64_t qhi = std::min<int64_t>(qlo + BM, b.lq);
+      const int64_t off = (int64_t)b.lk - b.lq;
+      const int64_t kmax = causal ? std::min<int64_t>(b.lk - 1, off + qhi - 1) : b.lk - 1;
+      const int64_t lim = causal ? std::min<int64_t>(b.lk - 1, off + qlo) : b.lk - 1;
+      ne = kmax >= 0 ? (int)(kmax / BN) + 1 : 0;
+      nf = (qlo + BM <= b.lq && lim >= 0) ? (int)((lim + 1) / BN) : 0;
     }
-    for (int i = nf + lane; i < t.n_kt; i += 64) t.full_idx[rowoff + i] = -1;
-    for (int i = np + lane; i < t.n_kt; i += 64) t.part_idx[rowoff + i] = -1;
-    if (lane == 0) {
-      t.full_cnt[row] = nf;
-      t.part_cnt[row] = np;
-      work[row] = nf + np;
-    }
+    nf_s[row] = nf;
+    np_s[row] = ne - nf;
+    t.full_cnt[row] = nf;
+    t.part_cnt[row] = ne - nf;
   }
   __syncthreads();
-  // Rank of row r: rows with more listed tiles, or as many and a lower index.
-  for (int r = tid; r < rows; r += kSmallThreads) {
-    const int my = work[r];
-    int rank = 0;
-    for (int k = 0; k < rows; ++k) {
-      const int w = work[k];
-      rank += (w > my) || (w == my && k < r);
-    }
-    t.row_order[rank] = r;
+  // Classes and lists: FULL entries 0..nf-1, PARTIAL entries nf..ne-1, the
+  // rest of each list -1.
+  const int total = rows * nkt;
+  for (int idx = tid; idx < total; idx += kSmallThreads) {
+    const int row = idx / nkt, j = idx - row * nkt;
+    const int nf = nf_s[row], np = np_s[row];
+    t.tile_class[idx] = j < nf ? BMATTN_TILE_FULL : (j < nf + np ? BMATTN_TILE_PARTIAL : BMATTN_TILE_EMPTY);
+    t.full_idx[idx] = j < nf ? j : -1;
+    t.part_idx[idx] = j < np ? nf + j : -1;
   }
+  // Rank of row r: rows with more listed tiles, or as many and a lower index;
+  // P threads per row each count over a slice of the rows.
+  const int P = rows < kSmallThreads ? kSmallThreads / rows : 1;
+  const int chunk = (rows + P - 1) / P;
+  for (int u = tid; u < rows * P; u += kSmallThreads) {
+    const int r = u / P, k0 = (u % P) * chunk, k1 = std::min(rows, k0 + chunk);
+    const int my = nf_s[r] + np_s[r];
+    int c = 0;
+    for (int k = k0; k < k1; ++k) {
+      const int w = nf_s[k] + np_s[k];
+      c += (w > my) || (w == my && k < r);
+    }
+    if (c) atomicAdd(&rank_s[r], c);
+  }
+  __syncthreads();
+  for (int r = tid; r < rows; r += kSmallThreads) t.row_order[rank_s[r]] = r;
 }
 
 __global__ __launch_bounds__(kThreads) void dense_mask_kernel(MaskDev m, TilesDev t, int seq,
