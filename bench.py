@@ -259,11 +259,24 @@ def main():
     fwd_ms = [a.elapsed_time(b) for a, b in evs]
     fwd_avg_ms = sum(fwd_ms) / len(fwd_ms)
 
-    # mask build alone (cacheable across steps; reported separately)
-    torch.cuda.synchronize()
-    tb = time.perf_counter()
-    for _ in range(args.steps):
-        bm.build_block_mask(desc, BM, BN, out=tiles)
+    # mask build alone (cacheable across steps; reported separately), launched
+    # the same way as the steps
+    def builds(n):
+        for _ in range(n):
+            bm.build_block_mask(desc, BM, BN, out=tiles)
+    if args.launch == "graph":
+        bgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(bgraph):
+            builds(graph_steps)
+        bgraph.replay()
+        torch.cuda.synchronize()
+        tb = time.perf_counter()
+        for _ in range(args.steps // graph_steps):
+            bgraph.replay()
+    else:
+        torch.cuda.synchronize()
+        tb = time.perf_counter()
+        builds(args.steps)
     torch.cuda.synchronize()
     build_ms = (time.perf_counter() - tb) * 1e3 / args.steps
 
