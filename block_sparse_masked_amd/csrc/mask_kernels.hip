@@ -20,33 +20,41 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxBlock = 1024;
 
-// Visible query rows of a tile for key j when every pair of the tile passes
-// the causal condition and lies inside the sequence.  qid holds the row ids
-// (segment or turn) of the tile's query rows, [qmin, qmax] their range.
-__device__ __forceinline__ int key_visible_rows(const MaskDev& m, const SeqBounds& b, int j,
-                                                const int32_t* qid, int nrows, int32_t qmin,
-                                                int32_t qmax) {
+// Key ids as the classifier keeps them, one int per key: the segment
+// (shared-prefix), or the turn of a think key and INT32_MAX for any other
+// key (strip-thinking: a key is hidden from query turn tq iff its value is
+// below tq).
+__device__ __forceinline__ int32_t staged_kid(const MaskDev& m, const SeqBounds& b, int j) {
+  if (m.kind == BMATTN_MASK_SHARED_PREFIX) return m.seg_k[b.k0 + j];
+  return m.role_k[b.k0 + j] == m.think_role ? m.turn_k[b.k0 + j] : INT32_MAX;
+}
+
+// Visible query rows of a tile for a key with staged id kv when every pair
+// of the tile passes the causal condition and lies inside the sequence.  qid
+// holds the row ids (segment or turn) of the tile's query rows, [qmin, qmax]
+// their range.
+__device__ __forceinline__ int key_visible_rows(const MaskDev& m, int32_t kv, const int32_t* qid,
+                                                int nrows, int32_t qmin, int32_t qmax) {
   if (m.kind == BMATTN_MASK_SHARED_PREFIX) {
-    int32_t sk = m.seg_k[b.k0 + j];
-    if (sk == 0) return nrows;
-    if (sk < qmin || sk > qmax) return 0;
+    if (kv == 0) return nrows;
+    if (kv < qmin || kv > qmax) return 0;
     if (qmin == qmax) return nrows;
     int c = 0;
-    for (int i = 0; i < nrows; ++i) c += (qid[i] == sk);
+    for (int i = 0; i < nrows; ++i) c += (qid[i] == kv);
     return c;
   }
   // STRIP_THINKING: hidden when the key is think and from an earlier turn.
-  if (m.role_k[b.k0 + j] != m.think_role) return nrows;
-  int32_t tk = m.turn_k[b.k0 + j];
-  if (tk >= qmax) return nrows;
-  if (tk < qmin) return 0;
+  if (kv >= qmax) return nrows;
+  if (kv < qmin) return 0;
   int c = 0;
-  for (int i = 0; i < nrows; ++i) c += (tk >= qid[i]);
+  for (int i = 0; i < nrows; ++i) c += (kv >= qid[i]);
   return c;
 }
 
+// kid[j - klo] is the staged id of key j of this tile (id-based kinds).
 __device__ uint8_t classify_tile(const MaskDev& m, const SeqBounds& b, int qlo, int klo, int BM,
-                                 int BN, const int32_t* qid, int32_t qmin, int32_t qmax) {
+                                 int BN, const int32_t* qid, int32_t qmin, int32_t qmax,
+                                 const int32_t* kid) {
   if (qlo >= b.lq || klo >= b.lk) return BMATTN_TILE_EMPTY;
   const int qhi = min(qlo + BM, b.lq);
   const int khi = min(klo + BN, b.lk);
@@ -62,8 +70,20 @@ __device__ uint8_t classify_tile(const MaskDev& m, const SeqBounds& b, int qlo, 
     // Only the id condition can hide pairs: count visible rows key by key.
     int64_t nvis = 0;
     bool hidden = false;
+    if (qmin == qmax) {
+      // One id for all the tile's query rows: a key is visible to all of
+      // them or to none, so the class follows from "every key" / "any key".
+      bool all = true, any = false;
+      for (int j = klo; j < khi; ++j) {
+        const int32_t kv = kid[j - klo];
+        const bool ok = m.kind == BMATTN_MASK_SHARED_PREFIX ? (kv == 0 || kv == qmin) : kv >= qmin;
+        all &= ok;
+        any |= ok;
+      }
+      return all ? BMATTN_TILE_FULL : (any ? BMATTN_TILE_PARTIAL : BMATTN_TILE_EMPTY);
+    }
     for (int j = klo; j < khi; ++j) {
-      int c = key_visible_rows(m, b, j, qid, BM, qmin, qmax);
+      int c = key_visible_rows(m, kid[j - klo], qid, BM, qmin, qmax);
       nvis += c;
       hidden |= (c < BM);
       if (nvis > 0 && hidden) return BMATTN_TILE_PARTIAL;
@@ -73,10 +93,27 @@ __device__ uint8_t classify_tile(const MaskDev& m, const SeqBounds& b, int qlo, 
   }
   // Diagonal or edge tile: enumerate the pairs (out-of-range pairs hidden).
   bool any_vis = false, any_hid = !inside;
+  const int64_t off2 = (int64_t)b.lk - b.lq;
+  auto vis = [&](int i, int j) -> bool {
+    // the element predicate on staged ids (pairs here are in range)
+    const int32_t kv = kid[j - klo], qv = qid[i - qlo];
+    const bool causal = (int64_t)j <= off2 + i;
+    return causal && (m.kind == BMATTN_MASK_SHARED_PREFIX ? (kv == 0 || kv == qv) : !(kv < qv));
+  };
+  // The four corners first: a visible and a hidden one settle the class.
+  {
+    const bool c0 = vis(qhi - 1, klo), c1 = vis(qlo, khi - 1), c2 = vis(qlo, klo), c3 = vis(qhi - 1, khi - 1);
+    any_vis = c0 | c1 | c2 | c3;
+    any_hid |= !(c0 & c1 & c2 & c3);
+    if (any_vis && any_hid) return BMATTN_TILE_PARTIAL;
+  }
   for (int j = klo; j < khi; ++j) {
+    const int32_t kv = kid[j - klo];
     for (int i = qlo; i < qhi; ++i) {
-      QIds q{qid[i - qlo], qid[i - qlo]};
-      bool v = visible(m, b, i, q, j);
+      // the element predicate on staged ids (pairs here are in range)
+      const int32_t qv = qid[i - qlo];
+      const bool causal = (int64_t)j <= off2 + i;
+      const bool v = causal && (m.kind == BMATTN_MASK_SHARED_PREFIX ? (kv == 0 || kv == qv) : !(kv < qv));
       any_vis |= v;
       any_hid |= !v;
       if (any_vis && any_hid) return BMATTN_TILE_PARTIAL;
@@ -88,8 +125,13 @@ __device__ uint8_t classify_tile(const MaskDev& m, const SeqBounds& b, int qlo, 
 
 // One workgroup per query-tile row: classifies the row's kv tiles in chunks
 // of 256 and appends FULL / PARTIAL indices in ascending order.
+// Staged key ids per chunk: tiles of BN keys, each run padded to BN + 1
+// words so that lanes scanning different tiles hit different LDS banks.
+constexpr int kKidKeys = 16384;
+
 __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev t) {
   __shared__ int32_t qid[kMaxBlock];
+  __shared__ int32_t kid[kKidKeys + kThreads];
   __shared__ int32_t wave_tot[2][kThreads / 64];
   __shared__ int32_t red[2][kThreads / 64];
   const int row = blockIdx.x;
@@ -127,11 +169,24 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev 
 
   const int64_t rowoff = (int64_t)row * t.n_kt;
   int full_base = 0, part_base = 0;
-  for (int c0 = 0; c0 < t.n_kt; c0 += kThreads) {
+  // Chunks of tpc kv tiles, one per thread; for the id-based kinds the ids of
+  // the chunk's keys are first staged in LDS with coalesced loads.
+  const bool ids = m.kind == BMATTN_MASK_SHARED_PREFIX || m.kind == BMATTN_MASK_STRIP_THINKING;
+  const int tpc = std::max(1, std::min(kThreads, kKidKeys / BN));
+  for (int c0 = 0; c0 < t.n_kt; c0 += tpc) {
     const int bidx = c0 + tid;
+    const int kid0 = c0 * BN;
+    if (ids) {
+      const int kend = (int)std::min<int64_t>((int64_t)(c0 + tpc) * BN, b.lk);
+      for (int j = kid0 + tid; j < kend; j += kThreads) {
+        const int u = j - kid0;
+        kid[u + u / BN] = staged_kid(m, b, j);
+      }
+      __syncthreads();
+    }
     uint8_t cls = BMATTN_TILE_EMPTY;
-    if (bidx < t.n_kt) {
-      cls = classify_tile(m, b, qlo, bidx * BN, BM, BN, qid, qmin, qmax);
+    if (tid < tpc && bidx < t.n_kt) {
+      cls = classify_tile(m, b, qlo, bidx * BN, BM, BN, qid, qmin, qmax, kid + tid * (BN + 1));
       t.tile_class[rowoff + bidx] = cls;
     }
     const uint64_t fm = __ballot(cls == BMATTN_TILE_FULL);
