@@ -16,6 +16,11 @@ Sources:
   express shared-prefix and strip-thinking multi-turn training that
   cu_seqlens cannot", section "Mask specifications": both predicates are the
   causal condition AND a condition on per-token ids.
+* strip_thinking_duplicated -- the same issue, section "The exactness
+  question", option (b): every answer span appears twice, a loss copy that
+  sees its own turn's thinking and a history copy that sees the context
+  inference has once the thinking is stripped; later turns see the history
+  copy only.
 * full -- no mask: Ch. 21, section 21.1's kernel before causal masking.
 """
 
@@ -29,12 +34,13 @@ def query_positions(Lq: int, Lk: int) -> np.ndarray:
     return np.arange(Lq, dtype=np.int64) + (Lk - Lq)
 
 
-def visible(kind: str, Lq: int, Lk: int, *, seg_q=None, seg_k=None, role_k=None,
-            turn_q=None, turn_k=None, think_role: int = 1) -> np.ndarray:
+def visible(kind: str, Lq: int, Lk: int, *, seg_q=None, seg_k=None, role_q=None, role_k=None,
+            turn_q=None, turn_k=None, think_role: int = 1, loss_role: int = 2,
+            history_role: int = 3) -> np.ndarray:
     """Dense boolean mask ``[Lq, Lk]`` for one sequence.
 
-    ``seg_q``/``turn_q`` are per query row, ``seg_k``/``role_k``/``turn_k``
-    per key; each kind reads only the ids it needs.
+    ``seg_q``/``role_q``/``turn_q`` are per query row, ``seg_k``/``role_k``/
+    ``turn_k`` per key; each kind reads only the ids it needs.
     """
     qi = query_positions(Lq, Lk)[:, None]
     kj = np.arange(Lk, dtype=np.int64)[None, :]
@@ -53,13 +59,46 @@ def visible(kind: str, Lq: int, Lk: int, *, seg_q=None, seg_k=None, role_k=None,
         rk = np.asarray(role_k, dtype=np.int64)[None, :]
         hidden = (rk == think_role) & (tk < tq)
         return causal & ~hidden
+    if kind == "strip_thinking_duplicated":
+        return causal & _duplicated_answer_context(role_q, role_k, turn_q, turn_k,
+                                                   think_role, loss_role, history_role)
     raise ValueError(f"unknown mask kind {kind!r}")
+
+
+def _duplicated_answer_context(role_q, role_k, turn_q, turn_k, think_role, loss_role,
+                               history_role) -> np.ndarray:
+    """Which keys lie in each query's context when answers are duplicated
+    (causality aside).
+
+    xorl issue, "The exactness question", option (b).  A finished turn
+    enters later turns the way inference replays it: its thinking is gone
+    and its answer is the history copy, so a key of an earlier turn is in
+    the context unless it is thinking or a loss copy.  Inside the query's
+    own turn the two answer copies see different things: the history copy
+    sees the turn stripped of its thinking (and of the loss copy, which
+    inference never holds beside it); every other token of the turn (user
+    text, thinking, the loss copy) sees the turn as generated, i.e. without
+    the history copy.  Keys of later turns are never in the context.
+    """
+    rq = np.asarray(role_q, dtype=np.int64)[:, None]
+    tq = np.asarray(turn_q, dtype=np.int64)[:, None]
+    rk = np.asarray(role_k, dtype=np.int64)[None, :]
+    tk = np.asarray(turn_k, dtype=np.int64)[None, :]
+    stripped_away = (rk == think_role) | (rk == loss_role)
+    query_is_history = rq == history_role
+    earlier = tk < tq
+    same_turn = tk == tq
+    from_history = earlier & ~stripped_away
+    own_turn_replayed = same_turn & query_is_history & ~stripped_away
+    own_turn_generated = same_turn & ~query_is_history & (rk != history_role)
+    return from_history | own_turn_replayed | own_turn_generated
 
 
 def visible_for_layout(layout, s: int) -> np.ndarray:
     """Dense mask of sequence ``s`` of a ``synth.Layout``."""
     ids = layout.ids_for_seq(s)
     return visible(layout.kind, layout.seqlens_q[s], layout.seqlens_k[s],
-                   seg_q=ids.get("seg_q"), seg_k=ids.get("seg_k"), role_k=ids.get("role_k"),
-                   turn_q=ids.get("turn_q"), turn_k=ids.get("turn_k"),
-                   think_role=layout.think_role)
+                   seg_q=ids.get("seg_q"), seg_k=ids.get("seg_k"), role_q=ids.get("role_q"),
+                   role_k=ids.get("role_k"), turn_q=ids.get("turn_q"), turn_k=ids.get("turn_k"),
+                   think_role=layout.think_role, loss_role=layout.loss_role,
+                   history_role=layout.history_role)

@@ -6,7 +6,11 @@ CPU oracle tests and the HIP path tests draw their inputs from this package.
 """
 
 from .workloads import (  # noqa: F401
+    USER_ROLE,
     THINK_ROLE,
+    ANSWER_ROLE,
+    LOSS_ROLE,
+    HISTORY_ROLE,
     KINDS,
     Layout,
     causal_single,
@@ -14,6 +18,7 @@ from .workloads import (  # noqa: F401
     packed_documents,
     shared_prefix,
     strip_thinking,
+    strip_thinking_duplicated,
     paged_decode,
     config,
     CONFIG_NAMES,

@@ -9,7 +9,8 @@ table into a page pool ``[num_pages, page_size, H, D]``).
 
 Per-token ids describe structure only:
   * ``seg``  -- segment id (0 = shared prefix, i >= 1 = the i-th suffix),
-  * ``role`` -- 0 user, 1 think, 2 answer,
+  * ``role`` -- 0 user, 1 think, 2 answer; with duplicated answers 2 is the
+    answer's loss copy and 3 its history copy,
   * ``turn`` -- conversation turn index.
 
 Random values are float32 standard normals drawn from a torch generator on the
@@ -25,8 +26,11 @@ from typing import Optional
 
 import numpy as np
 
+USER_ROLE = 0
 THINK_ROLE = 1
-KINDS = ("full", "causal", "shared_prefix", "strip_thinking")
+ANSWER_ROLE = LOSS_ROLE = 2
+HISTORY_ROLE = 3
+KINDS = ("full", "causal", "shared_prefix", "strip_thinking", "strip_thinking_duplicated")
 
 
 def derive_seed(seed: int, *tags: int) -> int:
@@ -51,10 +55,13 @@ class Layout:
     # q and k arrays are the same object.
     seg_q: Optional[np.ndarray] = None
     seg_k: Optional[np.ndarray] = None
+    role_q: Optional[np.ndarray] = None
     role_k: Optional[np.ndarray] = None
     turn_q: Optional[np.ndarray] = None
     turn_k: Optional[np.ndarray] = None
     think_role: int = THINK_ROLE
+    loss_role: int = LOSS_ROLE
+    history_role: int = HISTORY_ROLE
     paged: bool = False
     page_size: int = 16
     notes: dict = field(default_factory=dict)
@@ -102,7 +109,7 @@ class Layout:
         """The id slices that belong to sequence ``s`` (q-side and k-side)."""
         cq, ck = self.cu_q, self.cu_k
         out = {}
-        for name in ("seg_q", "turn_q"):
+        for name in ("seg_q", "role_q", "turn_q"):
             a = getattr(self, name)
             if a is not None:
                 out[name] = a[cq[s]:cq[s + 1]]
@@ -166,6 +173,26 @@ def strip_thinking(n_turns: int = 8, user: int = 256, think: int = 1536, answer:
                   notes={"n_turns": n_turns, "user": user, "think": think, "answer": answer})
 
 
+def strip_thinking_duplicated(n_turns: int = 8, user: int = 256, think: int = 1536,
+                              answer: int = 512, H: int = 32, D: int = 128,
+                              dtype: str = "bf16") -> Layout:
+    """n_turns of (user, think, answer loss copy, answer history copy) spans
+    packed in one sequence: the strip-thinking conversation with every
+    answer span written twice, the history copy right after the loss copy."""
+    roles, turns = [], []
+    for t in range(n_turns):
+        for r, n in ((USER_ROLE, user), (THINK_ROLE, think), (LOSS_ROLE, answer),
+                     (HISTORY_ROLE, answer)):
+            roles.append(np.full(n, r, np.int32))
+            turns.append(np.full(n, t, np.int32))
+    role = np.concatenate(roles)
+    turn = np.concatenate(turns)
+    T = int(role.size)
+    return Layout("strip_thinking_duplicated", "strip_thinking_duplicated", dtype, H, D, [T], [T],
+                  role_q=role, role_k=role, turn_q=turn, turn_k=turn,
+                  notes={"n_turns": n_turns, "user": user, "think": think, "answer": answer})
+
+
 def paged_decode(seed: int = 0, n_seqs: int = 64, lo: int = 512, hi: int = 32768,
                  page_size: int = 16, H: int = 32, D: int = 128, dtype: str = "bf16") -> Layout:
     """One new query per sequence over a paged context of ragged length."""
@@ -175,7 +202,8 @@ def paged_decode(seed: int = 0, n_seqs: int = 64, lo: int = 512, hi: int = 32768
                   paged=True, page_size=page_size, notes={"ctx": ctx})
 
 
-CONFIG_NAMES = ("causal_f32", "packed_documents", "shared_prefix", "strip_thinking", "paged_decode")
+CONFIG_NAMES = ("causal_f32", "packed_documents", "shared_prefix", "strip_thinking", "paged_decode",
+                "strip_thinking_duplicated")
 
 
 def config(name: str, seed: int = 0) -> Layout:
@@ -190,6 +218,8 @@ def config(name: str, seed: int = 0) -> Layout:
         return strip_thinking()
     if name == "paged_decode":
         return paged_decode(seed)
+    if name == "strip_thinking_duplicated":
+        return strip_thinking_duplicated()
     raise KeyError(name)
 
 
@@ -209,7 +239,7 @@ def random_layout(rng: np.random.Generator, kind: str, n_seqs: int = 3, max_len:
         lens_q = list(lens_k)
     else:
         lens_q = [min(decode_q, lk) for lk in lens_k]
-    seg_k = role_k = turn_k = seg_q = turn_q = None
+    seg_k = role_k = turn_k = seg_q = turn_q = role_q = None
     if kind == "shared_prefix":
         parts = []
         for L in lens_k:
@@ -240,6 +270,29 @@ def random_layout(rng: np.random.Generator, kind: str, n_seqs: int = 3, max_len:
             tparts.append(turn)
         role_k = np.concatenate(rparts).astype(np.int32) if rparts else np.zeros(0, np.int32)
         turn_k = np.concatenate(tparts).astype(np.int32) if tparts else np.zeros(0, np.int32)
+    elif kind == "strip_thinking_duplicated":
+        # turns of user, think, loss-copy and history-copy spans; the two
+        # answer copies have one length; the sequence may end inside a turn
+        rparts, tparts = [], []
+        for L in lens_k:
+            role = np.zeros(L, np.int32)
+            turn = np.zeros(L, np.int32)
+            pos = 0
+            t = 0
+            cap = max(2, L // (n_turns * 3) + 2)
+            while pos < L:
+                nu, nt, na = (int(x) for x in rng.integers(1, cap, size=3))
+                for r, n in ((USER_ROLE, nu), (THINK_ROLE, nt), (LOSS_ROLE, na), (HISTORY_ROLE, na)):
+                    role[pos:pos + n] = r
+                    turn[pos:pos + n] = t
+                    pos += n
+                    if pos >= L:
+                        break
+                t += 1
+            rparts.append(role)
+            tparts.append(turn)
+        role_k = np.concatenate(rparts).astype(np.int32) if rparts else np.zeros(0, np.int32)
+        turn_k = np.concatenate(tparts).astype(np.int32) if tparts else np.zeros(0, np.int32)
     # q-side ids: the last lens_q[s] key positions of each sequence.
     cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(int)
 
@@ -253,8 +306,11 @@ def random_layout(rng: np.random.Generator, kind: str, n_seqs: int = 3, max_len:
 
     seg_q = q_side(seg_k)
     turn_q = q_side(turn_k)
+    if kind == "strip_thinking_duplicated":
+        role_q = q_side(role_k)
     return Layout(f"random_{kind}", kind, dtype, H, D, lens_q, lens_k,
-                  seg_q=seg_q, seg_k=seg_k, role_k=role_k, turn_q=turn_q, turn_k=turn_k,
+                  seg_q=seg_q, seg_k=seg_k, role_q=role_q, role_k=role_k, turn_q=turn_q,
+                  turn_k=turn_k,
                   paged=paged, page_size=page_size)
 
 

@@ -163,3 +163,124 @@ def test_full_mask():
     assert masks.visible("full", 3, 5).all()
     with pytest.raises(ValueError):
         masks.visible("bogus", 2, 2)
+
+
+def _dup_visible(role, turn):
+    T = len(role)
+    return masks.visible("strip_thinking_duplicated", T, T, role_q=role, role_k=role, turn_q=turn,
+                         turn_k=turn, think_role=synth.THINK_ROLE, loss_role=synth.LOSS_ROLE,
+                         history_role=synth.HISTORY_ROLE)
+
+
+def test_duplicated_answers_match_hand_worked_12x12():
+    # xorl issue, "The exactness question", option (b), worked by hand.
+    g = _golden.load("strip_thinking_duplicated_12x12.txt")
+    role, turn = g["role"].astype(np.int32), g["turn"].astype(np.int32)
+    assert np.array_equal(_dup_visible(role, turn), g["visible"].astype(bool))
+    lay = synth.strip_thinking_duplicated(n_turns=2, user=1, think=1, answer=2, H=1, D=8)
+    assert np.array_equal(lay.role_k, role) and np.array_equal(lay.turn_k, turn)
+    assert np.array_equal(masks.visible_for_layout(lay, 0), g["visible"].astype(bool))
+
+
+def test_duplicated_answers_without_answers_is_strip_thinking():
+    # With no answer tokens there is nothing to duplicate: option (b) is the
+    # plain strip-thinking mask of the same sequence.
+    rng = np.random.default_rng(3)
+    for _ in range(4):
+        n = int(rng.integers(1, 30))
+        role = rng.choice([synth.USER_ROLE, synth.THINK_ROLE], size=n).astype(np.int32)
+        turn = np.sort(rng.integers(0, 4, size=n)).astype(np.int32)
+        plain = masks.visible("strip_thinking", n, n, role_k=role, turn_q=turn, turn_k=turn,
+                              think_role=synth.THINK_ROLE)
+        assert np.array_equal(_dup_visible(role, turn), plain)
+
+
+def _conversation(rng, n_turns, cap):
+    """Span lengths (user, think, answer) of each turn, answers non-empty."""
+    return [(int(rng.integers(1, cap)), int(rng.integers(0, cap)), int(rng.integers(1, cap)))
+            for _ in range(n_turns)]
+
+
+def _toy_network(x, vis, weights):
+    """Residual single-head attention layers, no positions: a token's state
+    depends only on the states of the keys it sees."""
+    from oracle import attention
+    for wq, wk, wv in weights:
+        o, _ = attention.three_pass(x @ wq, x @ wk, x @ wv, vis, 0.5)
+        x = x + o
+    return x
+
+
+def test_duplicated_answers_reproduce_inference_contexts():
+    # The point of option (b): with every answer duplicated, one packed pass
+    # gives each token the hidden states it has at inference, at every
+    # depth.  Inference of turn t runs plain causal attention over the
+    # conversation as replayed then: earlier turns without their thinking,
+    # then the current turn as generated.  The history copy of turn t must
+    # equal the answer of turn t replayed the same way.  Mask only (option
+    # (a), one copy per answer) matches at depth 1 and fails at depth 2.
+    rng = np.random.default_rng(17)
+    d, depth = 8, 2
+    diverged = 0
+    for trial in range(3):
+        conv = _conversation(rng, n_turns=int(rng.integers(2, 5)), cap=4)
+        n_tok = sum(u + th + a for u, th, a in conv)
+        emb = rng.standard_normal((n_tok, d))
+        weights = [tuple(rng.standard_normal((d, d)) * 0.7 for _ in range(3)) for _ in range(depth)]
+        ids = []  # per turn: token ids of the user, think and answer spans
+        nxt = 0
+        for u, th, a in conv:
+            ids.append([list(range(nxt, nxt + u)), list(range(nxt + u, nxt + u + th)),
+                        list(range(nxt + u + th, nxt + u + th + a))])
+            nxt += u + th + a
+        # the duplicated sequence and, per position, which copy it holds
+        seq, role, turn = [], [], []
+        for t, (us, ths, ans) in enumerate(ids):
+            for r, span in ((synth.USER_ROLE, us), (synth.THINK_ROLE, ths), (synth.LOSS_ROLE, ans),
+                            (synth.HISTORY_ROLE, ans)):
+                seq += span
+                role += [r] * len(span)
+                turn += [t] * len(span)
+        role, turn = np.array(role, np.int32), np.array(turn, np.int32)
+        packed = _toy_network(emb[seq], _dup_visible(role, turn), weights)
+
+        def run_causal(tokens):
+            return _toy_network(emb[tokens], masks.visible("causal", len(tokens), len(tokens)),
+                                weights)
+
+        for t, (us, ths, ans) in enumerate(ids):
+            replayed = [x for s in range(t) for x in ids[s][0] + ids[s][2]]
+            gen = run_causal(replayed + us + ths + ans)
+            n = len(replayed)
+            for r, span in ((synth.USER_ROLE, us), (synth.THINK_ROLE, ths), (synth.LOSS_ROLE, ans)):
+                at = np.nonzero((role == r) & (turn == t))[0]
+                where = [n + (us + ths + ans).index(x) for x in span]
+                np.testing.assert_allclose(packed[at], gen[where], rtol=0, atol=1e-12)
+            hist = run_causal(replayed + us + ans)
+            at = np.nonzero((role == synth.HISTORY_ROLE) & (turn == t))[0]
+            np.testing.assert_allclose(packed[at], hist[n + len(us):], rtol=0, atol=1e-12)
+
+        # option (a): one copy per answer, strip-thinking mask
+        seq_a = [x for us, ths, ans in ids for x in us + ths + ans]
+        role_a = np.array([r for us, ths, ans in ids for r, span in
+                           ((synth.USER_ROLE, us), (synth.THINK_ROLE, ths), (synth.ANSWER_ROLE, ans))
+                           for _ in span], np.int32)
+        turn_a = np.array([t for t, (us, ths, ans) in enumerate(ids) for _ in us + ths + ans],
+                          np.int32)
+        T = len(seq_a)
+        vis_a = masks.visible("strip_thinking", T, T, role_k=role_a, turn_q=turn_a, turn_k=turn_a)
+        last = len(ids) - 1
+        us, ths, ans = ids[last]
+        replayed = [x for s in range(last) for x in ids[s][0] + ids[s][2]]
+        gen = run_causal(replayed + us + ths + ans)
+        at = np.nonzero(turn_a == last)[0]
+        one_layer = lambda toks, vis: _toy_network(emb[toks], vis, weights[:1])
+        np.testing.assert_allclose(
+            one_layer(seq_a, vis_a)[at],
+            one_layer(replayed + us + ths + ans,
+                      masks.visible("causal", len(gen), len(gen)))[len(replayed):],
+            rtol=0, atol=1e-12)
+        if any(th > 0 for _, th, _ in conv[:last]):
+            assert np.abs(_toy_network(emb[seq_a], vis_a, weights)[at] - gen[len(replayed):]).max() > 1e-6
+            diverged += 1
+    assert diverged >= 1

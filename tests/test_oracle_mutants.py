@@ -165,3 +165,53 @@ def test_mutant_gather_reads_past_context(monkeypatch):
     import oracle.forward as of
     monkeypatch.setattr(of, "paged_gather", wrong)
     assert _fails(tp.test_ragged_rows_through_pages, tp.test_gather_byte_equal_for_every_tile_size) >= 1
+
+
+def _dup_mutant(monkeypatch, fn):
+    monkeypatch.setattr(masks, "_duplicated_answer_context", fn)
+    return _fails(tm.test_duplicated_answers_match_hand_worked_12x12,
+                  tm.test_duplicated_answers_reproduce_inference_contexts)
+
+
+def _dup_parts(role_q, role_k, turn_q, turn_k, think, loss, history):
+    rq = np.asarray(role_q)[:, None]
+    tq = np.asarray(turn_q)[:, None]
+    rk = np.asarray(role_k)[None, :]
+    tk = np.asarray(turn_k)[None, :]
+    return rq, tq, rk, tk
+
+
+def test_mutant_history_copy_sees_own_thinking(monkeypatch):
+    def wrong(role_q, role_k, turn_q, turn_k, think, loss, history):
+        rq, tq, rk, tk = _dup_parts(role_q, role_k, turn_q, turn_k, think, loss, history)
+        away = (rk == think) | (rk == loss)
+        return ((tk < tq) & ~away) | ((tk == tq) & (rq == history) & (rk != loss)) | \
+               ((tk == tq) & (rq != history) & (rk != history))
+    assert _dup_mutant(monkeypatch, wrong) >= 1
+
+
+def test_mutant_later_turns_see_loss_copy(monkeypatch):
+    def wrong(role_q, role_k, turn_q, turn_k, think, loss, history):
+        rq, tq, rk, tk = _dup_parts(role_q, role_k, turn_q, turn_k, think, loss, history)
+        away = (rk == think) | (rk == history)  # the copies swapped for history
+        return ((tk < tq) & ~away) | ((tk == tq) & (rq == history) & (rk != think) & (rk != loss)) | \
+               ((tk == tq) & (rq != history) & (rk != history))
+    assert _dup_mutant(monkeypatch, wrong) >= 1
+
+
+def test_mutant_history_copy_misses_own_user_text(monkeypatch):
+    def wrong(role_q, role_k, turn_q, turn_k, think, loss, history):
+        rq, tq, rk, tk = _dup_parts(role_q, role_k, turn_q, turn_k, think, loss, history)
+        away = (rk == think) | (rk == loss)
+        return ((tk < tq) & ~away) | ((tk == tq) & (rq == history) & (rk == history)) | \
+               ((tk == tq) & (rq != history) & (rk != history))
+    assert _dup_mutant(monkeypatch, wrong) >= 1
+
+
+def test_mutant_loss_copy_misses_own_thinking(monkeypatch):
+    def wrong(role_q, role_k, turn_q, turn_k, think, loss, history):
+        rq, tq, rk, tk = _dup_parts(role_q, role_k, turn_q, turn_k, think, loss, history)
+        away = (rk == think) | (rk == loss)
+        return ((tk < tq) & ~away) | ((tk == tq) & (rq == history) & ~away) | \
+               ((tk == tq) & (rq != history) & (rk != history) & ~((rq == loss) & (rk == think)))
+    assert _dup_mutant(monkeypatch, wrong) >= 1
