@@ -10,7 +10,9 @@ head (2*D for Q K^T, 2*D for P V).  Prints one JSON line.
 
 The default workload is the packed-document batch (8 causal documents with
 lengths uniform in [64, 2048], 16 heads, head_dim 128, bf16).  Other named
-workloads: causal_f32, shared_prefix, strip_thinking, paged_decode.
+workloads: causal_f32, shared_prefix, strip_thinking, paged_decode,
+strip_thinking_duplicated (whose step starts with the relabelling of its ids,
+bmattn_duplicated_answer_ids).
 """
 
 from __future__ import annotations
@@ -47,6 +49,16 @@ def visible_pairs(lay) -> int:
             b = t * T
             # a query at position p of turn t sees p + 1 keys minus t think spans
             tot += (T * (2 * b + T + 1)) // 2 - T * t * th
+        return tot
+    if lay.name == "strip_thinking_duplicated":
+        u, th, a, n = (lay.notes[k] for k in ("user", "think", "answer", "n_turns"))
+        tot = 0
+        for t in range(n):
+            hist = t * (u + a)  # earlier turns: user text and history copies
+            n1 = u + th + a     # user, think, loss copy: the turn as generated
+            tot += n1 * hist + n1 * (n1 + 1) // 2
+            # history copy: earlier turns, its own user text, itself causally
+            tot += a * (hist + u) + a * (a + 1) // 2
         return tot
     if lay.kind == "full":
         return sum(q * k for q, k in zip(lay.seqlens_q, lay.seqlens_k))
@@ -114,14 +126,12 @@ def cpu_baseline(lay, q, k, v, kp, vp, bt, flops_total: float, budget_s: float =
                 "sample": f"{passes} of {lay.n_seqs} sequences x heads 0-3 (float64 numpy), {dt:.1f} s"}
     qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
     passes, t0 = 0, time.perf_counter()
-    if lay.name in ("shared_prefix", "strip_thinking"):
+    if lay.name in ("shared_prefix", "strip_thinking", "strip_thinking_duplicated"):
         # One head per pass of the single long sequence.
+        import dataclasses
+        one_head = dataclasses.replace(lay, num_heads=1)
         for h in range(lay.num_heads):
-            sub_q = qc[:, h:h + 1]
-            oforward.forward(type(lay)(lay.name, lay.kind, lay.dtype, 1, lay.head_dim, lay.seqlens_q,
-                                       lay.seqlens_k, seg_q=lay.seg_q, seg_k=lay.seg_k,
-                                       role_k=lay.role_k, turn_q=lay.turn_q, turn_k=lay.turn_k),
-                             sub_q, kc[:, h:h + 1], vc[:, h:h + 1])
+            oforward.forward(one_head, qc[:, h:h + 1], kc[:, h:h + 1], vc[:, h:h + 1])
             passes += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
@@ -196,8 +206,15 @@ def main():
     else:
         q, k, v = synth.make_dense_qkv(lay, seed=args.seed, device=dev)
     desc = bm.MaskDesc.create(lay.kind, lay.cu_q, lay.cu_k, lay.max_q, lay.max_k, device=dev,
-                              seg_q=lay.seg_q, seg_k=lay.seg_k, role_k=lay.role_k,
-                              turn_q=lay.turn_q, turn_k=lay.turn_k, think_role=lay.think_role)
+                              seg_q=lay.seg_q, seg_k=lay.seg_k, role_q=lay.role_q,
+                              role_k=lay.role_k, turn_q=lay.turn_q, turn_k=lay.turn_k,
+                              think_role=lay.think_role, loss_role=lay.loss_role,
+                              history_role=lay.history_role)
+    relabel = desc.duplicated_from is not None
+    if relabel:
+        flags = bm.relabel(desc, check=True)
+        if int(flags.item()) != 0:
+            raise SystemExit(f"[bench] duplicated-answer layout check failed: {int(flags.item())}")
     BM, BN = (1, 64) if lay.max_q == 1 else (128, 64)
     tiles = bm.build_block_mask(desc, BM, BN)
     out = torch.empty_like(q)
@@ -206,6 +223,8 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
 
     def step(ev=None):
+        if relabel:
+            bm.relabel(desc)
         bm.build_block_mask(desc, BM, BN, out=tiles)
         if ev is not None:
             ev[0].record()
@@ -263,6 +282,8 @@ def main():
     # the same way as the steps
     def builds(n):
         for _ in range(n):
+            if relabel:
+                bm.relabel(desc)
             bm.build_block_mask(desc, BM, BN, out=tiles)
     if args.launch == "graph":
         bgraph = torch.cuda.CUDAGraph()

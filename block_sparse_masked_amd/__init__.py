@@ -7,7 +7,10 @@ include/bmattn.h); ``bmattn`` is its ctypes binding.  Build it with
 
 from . import bmattn  # noqa: F401
 
-bmattn.lib()  # fail loudly at import when the HIP library is not built
+# The library is loaded on first use: every entry point raises ImportError
+# when it is not built (or lacks a symbol), and nothing else runs in its
+# place.  Loading it here would keep `python -m block_sparse_masked_amd.build`
+# from running over a missing or stale library.
 from .bmattn import (  # noqa: F401
     BlockMask,
     BmattnError,

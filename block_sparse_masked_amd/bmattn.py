@@ -3,8 +3,9 @@
 Every step of the computation runs in the HIP library.  PyTorch provides
 device memory and the current stream; this module only fills the C structs
 declared in include/bmattn.h, allocates outputs with torch, and raises
-``BmattnError`` on a non-zero status.  If the built library is missing the
-import fails loudly: there is no other implementation behind these names.
+``BmattnError`` on a non-zero status.  If the built library is missing (or
+lacks a symbol) the first call raises ImportError: there is no other
+implementation behind these names.
 """
 
 from __future__ import annotations
@@ -29,7 +30,8 @@ STATUS = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "EALIGN", 4: "EHIP", 5: "E
 
 EXPORTS = ("bmattn_block_mask_shape", "bmattn_build_block_mask", "bmattn_forward_workspace_size",
            "bmattn_forward", "bmattn_paged_gather", "bmattn_debug_dense_mask", "bmattn_validate",
-           "bmattn_status_string", "bmattn_last_error", "bmattn_abi_version")
+           "bmattn_duplicated_answer_ids", "bmattn_status_string", "bmattn_last_error",
+           "bmattn_abi_version")
 
 _p = ctypes.c_void_p
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -103,6 +105,8 @@ def lib():
                                               ctypes.c_int32, _p, ctypes.c_int64, _p]
         L.bmattn_validate.argtypes = [ctypes.POINTER(MaskDescC), _p, ctypes.c_int64, ctypes.c_int32,
                                       ctypes.c_int64, _p, _p]
+        L.bmattn_duplicated_answer_ids.argtypes = [ctypes.POINTER(MaskDescC), _p, ctypes.c_int32,
+                                                   ctypes.c_int32, _p, _p, _p, _p]
         for name in EXPORTS:
             getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int
         _LIB = L
@@ -149,11 +153,25 @@ class MaskDesc:
     turn_q: Optional[torch.Tensor] = None
     turn_k: Optional[torch.Tensor] = None
     think_role: int = 1
+    # For a description relabelled from duplicated answers: (the description
+    # with the layout's own ids, role_q, loss_role, history_role).
+    duplicated_from: Optional[tuple] = None
 
     @staticmethod
     def create(kind, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, *,
-               device="cuda", seg_q=None, seg_k=None, role_k=None, turn_q=None, turn_k=None,
-               think_role: int = 1) -> "MaskDesc":
+               device="cuda", seg_q=None, seg_k=None, role_q=None, role_k=None, turn_q=None,
+               turn_k=None, think_role: int = 1, loss_role: int = 2,
+               history_role: int = 3) -> "MaskDesc":
+        """A description; kind "strip_thinking_duplicated" takes the ids of a
+        layout with duplicated answer spans (role_q, role_k with loss_role
+        and history_role, turn_q, turn_k) and returns the STRIP_THINKING
+        description that bmattn_duplicated_answer_ids relabels them to."""
+        if kind == "strip_thinking_duplicated":
+            src = MaskDesc.create("strip_thinking", cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                                  max_seqlen_k, device=device, role_k=role_k, turn_q=turn_q,
+                                  turn_k=turn_k, think_role=think_role)
+            return duplicated_answer_ids(src, _i32(role_q, device), loss_role=loss_role,
+                                         history_role=history_role)[0]
         kind = KIND_CODES[kind] if isinstance(kind, str) else int(kind)
         cq = _i32(cu_seqlens_q, device)
         ck = _i32(cu_seqlens_k, device)
@@ -313,6 +331,37 @@ def validate(desc: MaskDesc, block_table=None, page_size: int = 0, num_pages: in
                                  int(page_size), int(num_pages), _ptr(flags), _stream(stream)),
            "bmattn_validate")
     return int(flags.item())
+
+
+def duplicated_answer_ids(desc: MaskDesc, role_q: torch.Tensor, *, loss_role: int = 2,
+                          history_role: int = 3, out: Optional[MaskDesc] = None,
+                          check: bool = False, stream=None):
+    """bmattn_duplicated_answer_ids.  ``desc`` is a STRIP_THINKING description
+    holding the ids of a layout with duplicated answer spans; returns
+    (relabelled description, flags) where flags is a device int32 [1] tensor
+    (0 = the layout meets the conditions) when ``check``, else None.  With
+    ``out`` (a description from an earlier call on the same layout) the ids
+    are rewritten into its arrays."""
+    if out is None:
+        out = MaskDesc(desc.kind, desc.n_seqs, desc.max_seqlen_q, desc.max_seqlen_k, desc.total_q,
+                       desc.total_k, desc.cu_seqlens_q, desc.cu_seqlens_k, None, None,
+                       torch.empty_like(desc.role_k), torch.empty_like(desc.turn_q), desc.turn_k,
+                       desc.think_role, (desc, role_q, int(loss_role), int(history_role)))
+    flags = torch.empty(1, dtype=torch.int32, device=role_q.device) if check else None
+    d = desc.c()
+    _check(lib().bmattn_duplicated_answer_ids(ctypes.byref(d), _ptr(role_q), int(loss_role),
+                                              int(history_role), _ptr(out.role_k), _ptr(out.turn_q),
+                                              _ptr(flags), _stream(stream)),
+           "bmattn_duplicated_answer_ids")
+    return out, flags
+
+
+def relabel(desc: MaskDesc, check: bool = False, stream=None):
+    """Reruns the relabelling of a description made from duplicated answers
+    (into its own arrays); returns the flags tensor when ``check``."""
+    src, role_q, loss_role, history_role = desc.duplicated_from
+    return duplicated_answer_ids(src, role_q, loss_role=loss_role, history_role=history_role,
+                                 out=desc, check=check, stream=stream)[1]
 
 
 def default_scale(head_dim: int) -> float:

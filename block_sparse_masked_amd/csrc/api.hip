@@ -351,4 +351,24 @@ int bmattn_validate(const bmattn_mask_desc* desc, const int32_t* block_table,
   return BMATTN_OK;
 }
 
+int bmattn_duplicated_answer_ids(const bmattn_mask_desc* desc, const int32_t* role_q,
+                                 int32_t loss_role, int32_t history_role, int32_t* role_k_out,
+                                 int32_t* turn_q_out, int32_t* flags, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (desc->kind != BMATTN_MASK_STRIP_THINKING)
+    return fail(BMATTN_EINVAL, "duplicated answers need a STRIP_THINKING description");
+  if (role_q == nullptr || role_k_out == nullptr || turn_q_out == nullptr)
+    return fail(BMATTN_EINVAL, "role_q, role_k_out and turn_q_out must be non-NULL");
+  if (loss_role == history_role || loss_role == desc->think_role ||
+      history_role == desc->think_role)
+    return fail(BMATTN_EINVAL, "think, loss and history roles must differ (%d, %d, %d)",
+                desc->think_role, loss_role, history_role);
+  hipError_t e = launch_duplicated_answer_ids(to_dev(desc), desc->max_seqlen_q, desc->max_seqlen_k,
+                                              role_q, loss_role, history_role, role_k_out,
+                                              turn_q_out, flags, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bmattn_duplicated_answer_ids launch");
+  return BMATTN_OK;
+}
+
 }  // extern "C"

@@ -56,6 +56,10 @@ hipError_t launch_debug_dense_mask(const MaskDev& m, const TilesDev& t, int seq,
 hipError_t launch_validate(const MaskDev& m, int32_t max_lq, int32_t max_lk,
                            const int32_t* block_table, int64_t bt_stride, int32_t page_size,
                            int64_t num_pages, int32_t* flags, hipStream_t st);
+hipError_t launch_duplicated_answer_ids(const MaskDev& m, int32_t max_lq, int32_t max_lk,
+                                        const int32_t* role_q, int32_t loss_role,
+                                        int32_t history_role, int32_t* role_k_out,
+                                        int32_t* turn_q_out, int32_t* flags, hipStream_t st);
 hipError_t launch_paged_gather(const MaskDev& m, int32_t max_lk, const void* pool, int64_t st_tok,
                                int64_t st_head, int32_t elem_bytes, int32_t H, int32_t D,
                                int32_t page_size, int64_t num_pages, const int32_t* block_table,

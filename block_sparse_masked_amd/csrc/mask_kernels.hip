@@ -374,6 +374,67 @@ __global__ __launch_bounds__(kThreads) void validate_kernel(MaskDev m, int32_t m
   }
 }
 
+// Strip-thinking with duplicated answers (xorl issue, "The exactness
+// question", option (b)): checks, per sequence, the layout under which the
+// relabelled ids are exact.  One workgroup; wave w takes sequences w, w + 16,
+// ...; its lanes walk the sequence's keys (adjacent pairs) and queries.
+constexpr int kDupCheckThreads = 1024;
+
+__global__ __launch_bounds__(kDupCheckThreads) void duplicated_check_kernel(
+    MaskDev m, int32_t max_lq, int32_t max_lk, const int32_t* role_q, int32_t history_role,
+    int32_t* flags) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kWaves = kDupCheckThreads / 64;
+  int f = 0;
+  for (int s = wave; s < m.n_seqs; s += kWaves) {
+    const SeqBounds b = seq_bounds(m, s, max_lq, max_lk);
+    for (int j = lane; j + 1 < b.lk; j += 64) {
+      const int64_t a = b.k0 + j;
+      const int32_t t0 = m.turn_k[a], t1 = m.turn_k[a + 1];
+      if (t1 < t0) f |= 1;
+      else if (t1 == t0 && m.role_k[a] == history_role && m.role_k[a + 1] != history_role) f |= 2;
+    }
+    for (int i = lane; i < b.lq; i += 64) {
+      const int64_t qi = b.q0 + i;
+      const int64_t pos = (int64_t)b.lk - b.lq + i;  // the query's key position
+      const int32_t r = role_q[qi], t = m.turn_q[qi];
+      if (pos >= 0 && (r != m.role_k[b.k0 + pos] || t != m.turn_k[b.k0 + pos])) f |= 4;
+      if (r == history_role && t == INT32_MAX) f |= 8;
+    }
+  }
+  __shared__ int32_t red[kWaves];
+  for (int o = 32; o > 0; o >>= 1) f |= __shfl_xor(f, o);
+  if (lane == 0) red[wave] = f;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int tot = 0;
+    for (int w = 0; w < kWaves; ++w) tot |= red[w];
+    flags[0] = tot;
+  }
+}
+
+// The relabelling itself, one id per thread: a loss-copy key takes the think
+// role, a history-copy query's turn goes up by one (saturating; the check
+// reports INT32_MAX).  In place is allowed: each element is read before it
+// is written by the same thread.
+__global__ __launch_bounds__(kThreads) void duplicated_ids_kernel(
+    const int32_t* role_k, const int32_t* role_q, const int32_t* turn_q, int64_t total_k,
+    int64_t total_q, int32_t think_role, int32_t loss_role, int32_t history_role,
+    int32_t* role_k_out, int32_t* turn_q_out) {
+  const int64_t n = total_k > total_q ? total_k : total_q;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
+    if (i < total_k) {
+      const int32_t r = role_k[i];
+      role_k_out[i] = r == loss_role ? think_role : r;
+    }
+    if (i < total_q) {
+      const int32_t t = turn_q[i];
+      turn_q_out[i] = t + ((role_q[i] == history_role && t < INT32_MAX) ? 1 : 0);
+    }
+  }
+}
+
 __device__ __forceinline__ int32_t page_shift_of_dev(int32_t page_size) {
   return (page_size & (page_size - 1)) == 0 ? __builtin_ctz((uint32_t)page_size) : -1;
 }
@@ -431,6 +492,25 @@ hipError_t launch_validate(const MaskDev& m, int32_t max_lq, int32_t max_lk,
                            int64_t num_pages, int32_t* flags, hipStream_t st) {
   hipLaunchKernelGGL(validate_kernel, dim3(1), dim3(kThreads), 0, st, m, max_lq, max_lk,
                      block_table, bt_stride, page_size, num_pages, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_duplicated_answer_ids(const MaskDev& m, int32_t max_lq, int32_t max_lk,
+                                        const int32_t* role_q, int32_t loss_role,
+                                        int32_t history_role, int32_t* role_k_out,
+                                        int32_t* turn_q_out, int32_t* flags, hipStream_t st) {
+  if (flags != nullptr) {
+    hipLaunchKernelGGL(duplicated_check_kernel, dim3(1), dim3(kDupCheckThreads), 0, st, m, max_lq,
+                       max_lk, role_q, history_role, flags);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t n = m.total_k > m.total_q ? m.total_k : m.total_q;
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + kThreads - 1) / kThreads, 4096);
+  hipLaunchKernelGGL(duplicated_ids_kernel, dim3((uint32_t)blocks), dim3(kThreads), 0, st, m.role_k,
+                     role_q, m.turn_q, m.total_k, m.total_q, m.think_role, loss_role, history_role,
+                     role_k_out, turn_q_out);
   return hipGetLastError();
 }
 

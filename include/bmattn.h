@@ -234,6 +234,39 @@ int bmattn_validate(const bmattn_mask_desc* desc, const int32_t* block_table,
                     int64_t block_table_stride, int32_t page_size, int64_t num_pages,
                     int32_t* flags, void* stream);
 
+/* ---- strip-thinking with duplicated answers ------------------------------
+ * [XORL "The exactness question", option (b)].  The conversation is packed
+ * with every answer span written twice: a loss copy, which sees its own
+ * turn's thinking, and right after it a history copy, which sees its turn
+ * with the thinking stripped; later turns see the history copy and neither
+ * the thinking nor the loss copy.  With roles think_role (desc), loss_role
+ * and history_role marking those tokens, this call writes ids under which
+ * the STRIP_THINKING kind yields exactly that mask:
+ *   role_k_out[j] = think_role       if role_k[j] == loss_role, else role_k[j]
+ *   turn_q_out[i] = turn_q[i] + 1    if role_q[i] == history_role, else turn_q[i]
+ * (a loss copy is hidden from later turns as thinking is; a history-copy
+ * query hides its own turn's thinking and loss copy as if they were one turn
+ * earlier).  Build and run the forward with a STRIP_THINKING description
+ * whose role_k is role_k_out, turn_q is turn_q_out and turn_k is unchanged.
+ *
+ * desc: kind STRIP_THINKING holding the duplicated layout's ids (role_k,
+ * turn_q, turn_k, think_role).  role_q: [total_q] role of each query.
+ * Outputs: role_k_out [total_k], turn_q_out [total_q], device int32; they may
+ * be the input arrays themselves (rewritten in place).  think_role,
+ * loss_role and history_role must differ (else BMATTN_EINVAL).
+ *
+ * The relabelling is exact when, in every sequence, turns never decrease
+ * along the keys, a turn's history-copy tokens come after all its other
+ * tokens, a query carries the ids of the key at its position, and no
+ * history copy has turn INT32_MAX.  flags (device int32, may be NULL): when
+ * given, those conditions are checked on the device first and one word is
+ * written: bit 0 a turn decreases, bit 1 a non-history token follows a
+ * history copy of its turn, bit 2 a query's ids differ from its position's
+ * key, bit 3 a history copy at turn INT32_MAX; 0 means exact. */
+int bmattn_duplicated_answer_ids(const bmattn_mask_desc* desc, const int32_t* role_q,
+                                 int32_t loss_role, int32_t history_role, int32_t* role_k_out,
+                                 int32_t* turn_q_out, int32_t* flags, void* stream);
+
 /* Status text; thread-local last error text; ABI version. */
 const char* bmattn_status_string(int status);
 const char* bmattn_last_error(void);

@@ -26,8 +26,10 @@ def say(*a):
 def desc_for(layout, device=DEV) -> bm.MaskDesc:
     return bm.MaskDesc.create(layout.kind, layout.cu_q, layout.cu_k, max(layout.max_q, 1),
                               max(layout.max_k, 1), device=device, seg_q=layout.seg_q,
-                              seg_k=layout.seg_k, role_k=layout.role_k, turn_q=layout.turn_q,
-                              turn_k=layout.turn_k, think_role=layout.think_role)
+                              seg_k=layout.seg_k, role_q=layout.role_q, role_k=layout.role_k,
+                              turn_q=layout.turn_q, turn_k=layout.turn_k,
+                              think_role=layout.think_role, loss_role=layout.loss_role,
+                              history_role=layout.history_role)
 
 
 def oracle_tiles(layout, BM, BN):

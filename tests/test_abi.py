@@ -177,3 +177,29 @@ def test_gather_and_debug_and_validate_rejections():
     assert L.bmattn_debug_dense_mask(ctypes.byref(d), ctypes.byref(t), 0, FAKE, 3, None) == 1
     assert L.bmattn_validate(ctypes.byref(d), None, 0, 0, 0, None, None) == 1
     assert L.bmattn_validate(ctypes.byref(d), FAKE, 0, 16, 10, FAKE, None) == 1
+
+
+def test_duplicated_answer_ids_rejected_before_launch():
+    L = bm.lib()
+    f = ctypes.c_void_p(FAKE)
+
+    def call(d, role_q=f, loss=2, hist=3, rk=f, tq=f):
+        return L.bmattn_duplicated_answer_ids(ctypes.byref(d), role_q, loss, hist, rk, tq, None, None)
+
+    assert call(_desc(kind=bm.MASK_CAUSAL)) == 1          # not a STRIP_THINKING description
+    assert call(_desc(kind=bm.MASK_STRIP_THINKING, ids=False)) == 1  # its ids missing
+    st = _desc(kind=bm.MASK_STRIP_THINKING)
+    assert call(st, role_q=None) == 1
+    assert call(st, rk=None) == 1 and call(st, tq=None) == 1
+    assert call(st, loss=3, hist=3) == 1                  # roles must differ
+    assert call(st, loss=1) == 1 and call(st, hist=1) == 1  # think_role is 1
+    assert b"roles must differ" in L.bmattn_last_error()
+
+
+def test_missing_library_fails_loudly_on_first_call(tmp_path, monkeypatch):
+    # No fallback: with the library path pointing nowhere, a call raises.
+    from block_sparse_masked_amd import bmattn
+    monkeypatch.setattr(bmattn, "LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(bmattn, "_LIB", None)
+    with pytest.raises(ImportError):
+        bmattn.lib()

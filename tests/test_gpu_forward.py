@@ -132,14 +132,17 @@ def _sample_rows(T, rng, extra=()):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("name", ["shared_prefix", "strip_thinking"])
+@pytest.mark.parametrize("name", ["shared_prefix", "strip_thinking", "strip_thinking_duplicated"])
 def test_single_sequence_workloads_sampled(name):
     lay = synth.config(name)
     say(f"forward {name} full size")
     o, lse, q, k, v, desc, t = _hip.run_dense(lay, seed=0)
     rng = np.random.default_rng(5)
     T = lay.total_q
-    boundaries = [4095, 4096, 4097, 5119, 5120] if name == "shared_prefix" else [255, 256, 1791, 1792, 2303, 2304]
+    boundaries = {"shared_prefix": [4095, 4096, 4097, 5119, 5120],
+                  "strip_thinking": [255, 256, 1791, 1792, 2303, 2304],
+                  "strip_thinking_duplicated": [255, 256, 1791, 1792, 2303, 2304, 2815, 2816,
+                                                2817, 19711, 19712]}[name]
     rows = _sample_rows(T, rng, boundaries)
     on, ln = o.float().cpu().numpy(), lse.cpu().numpy()
     worst = 0.0

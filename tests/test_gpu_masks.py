@@ -16,7 +16,8 @@ pytestmark = pytest.mark.gpu
 
 SHAPES = [(1, 1), (2, 3), (4, 4), (13, 8), (16, 64), (64, 16), (128, 64), (1, 64), (37, 29),
           (128, 128), (256, 64)]
-KIND_SEED = {"full": 1, "causal": 2, "shared_prefix": 3, "strip_thinking": 4}
+KIND_SEED = {"full": 1, "causal": 2, "shared_prefix": 3, "strip_thinking": 4,
+             "strip_thinking_duplicated": 5}
 
 
 @pytest.mark.parametrize("decode_q", [None, 1, 3])
@@ -42,7 +43,7 @@ def test_tiles_empty_and_tiny_sequences():
 
 
 @pytest.mark.parametrize("name", ["causal_f32", "packed_documents", "shared_prefix",
-                                  "strip_thinking"])
+                                  "strip_thinking", "strip_thinking_duplicated"])
 def test_tiles_bit_exact_named_workloads(name):
     lay = synth.config(name)
     desc = _hip.desc_for(lay)
@@ -117,3 +118,84 @@ def test_paged_gather_byte_equal_decode_contexts():
     for s in range(lay.n_seqs):
         want = opaged.paged_gather(raw, bt[s].numpy(), lay.seqlens_k[s], 16)
         assert want.tobytes() == got[cu[s]:cu[s + 1]].tobytes(), s
+
+
+def _dup_flags(lay):
+    src = bm.MaskDesc.create("strip_thinking", lay.cu_q, lay.cu_k, max(lay.max_q, 1),
+                             max(lay.max_k, 1), device=DEV, role_k=lay.role_k, turn_q=lay.turn_q,
+                             turn_k=lay.turn_k)
+    role_q = torch.as_tensor(lay.role_q, dtype=torch.int32, device=DEV)
+    _, flags = bm.duplicated_answer_ids(src, role_q, check=True)
+    return int(flags.item())
+
+
+def test_duplicated_answer_layout_flags():
+    # The device check of the layout conditions under which the relabelled
+    # ids are exact: 0 on well-formed layouts, one bit per broken condition.
+    rng = np.random.default_rng(21)
+    for dq in (None, 2):
+        lay = synth.random_layout(rng, "strip_thinking_duplicated", n_seqs=20, max_len=300,
+                                  decode_q=dq)
+        say(f"duplicated flags: well-formed decode_q={dq}")
+        assert _dup_flags(lay) == 0
+    lay = synth.strip_thinking_duplicated(n_turns=3, user=2, think=3, answer=2, H=1, D=8)
+
+    def broken(**ids):
+        base = dict(role_q=lay.role_q.copy(), role_k=lay.role_k.copy(), turn_q=lay.turn_q.copy(),
+                    turn_k=lay.turn_k.copy())
+        for name, fn in ids.items():
+            base[name] = fn(base[name])
+        return synth.Layout("b", "strip_thinking_duplicated", "f32", 1, 8, lay.seqlens_q,
+                            lay.seqlens_k, **base)
+
+    def dec_turn(t):
+        t = t.copy()
+        t[-1] = 0
+        return t
+
+    def hist_first(r):
+        r = r.copy()
+        h = np.nonzero(r == synth.HISTORY_ROLE)[0]
+        r[h[0]], r[h[0] - 1] = r[h[0] - 1], r[h[0]]  # history copy before a loss-copy token
+        return r
+
+    def q_other(r):
+        r = r.copy()
+        r[0] = synth.THINK_ROLE
+        return r
+
+    def max_turn(t):
+        t = t.copy()
+        t[-1] = np.iinfo(np.int32).max
+        return t
+
+    say("duplicated flags: broken layouts")
+    assert _dup_flags(broken(turn_k=dec_turn, turn_q=dec_turn)) == 1
+    assert _dup_flags(broken(role_k=hist_first, role_q=hist_first)) == 2
+    assert _dup_flags(broken(role_q=q_other)) == 4
+    assert _dup_flags(broken(turn_q=max_turn, turn_k=max_turn)) == 8
+
+
+def test_duplicated_answer_ids_in_place():
+    rng = np.random.default_rng(8)
+    lay = synth.random_layout(rng, "strip_thinking_duplicated", n_seqs=3, max_len=200)
+    d1 = _hip.desc_for(lay)
+    src = bm.MaskDesc.create("strip_thinking", lay.cu_q, lay.cu_k, lay.max_q, lay.max_k, device=DEV,
+                             role_k=lay.role_k, turn_q=lay.turn_q, turn_k=lay.turn_k)
+    role_q = torch.as_tensor(lay.role_q, dtype=torch.int32, device=DEV)
+    rk, tq = src.role_k.clone(), src.turn_q.clone()
+    say("duplicated ids in place")
+    dst = bm.MaskDesc(src.kind, src.n_seqs, src.max_seqlen_q, src.max_seqlen_k, src.total_q,
+                      src.total_k, src.cu_seqlens_q, src.cu_seqlens_k, None, None, src.role_k,
+                      src.turn_q, src.turn_k, src.think_role)
+    bm.duplicated_answer_ids(src, role_q, out=dst)
+    torch.cuda.synchronize()
+    assert torch.equal(dst.role_k, d1.role_k) and torch.equal(dst.turn_q, d1.turn_q)
+    assert not torch.equal(rk, dst.role_k) and not torch.equal(tq, dst.turn_q)
+    # rerunning into a description's own arrays reproduces them
+    before = (d1.role_k.clone(), d1.turn_q.clone())
+    d1.role_k.fill_(-5)
+    d1.turn_q.fill_(-5)
+    bm.relabel(d1)
+    torch.cuda.synchronize()
+    assert torch.equal(d1.role_k, before[0]) and torch.equal(d1.turn_q, before[1])
