@@ -1,4 +1,4 @@
-"""CPU oracle for block-sparse masked attention (forward).
+"""CPU oracle for block-sparse masked attention (forward and backward).
 
 TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the package's
 smoke check and the benchmark's CPU-baseline leg may import, call or execute
@@ -17,10 +17,12 @@ Everything is float64 numpy on the host, written as the plain definition:
                    variant used only to pin block-size independence.
 * ``paged``     -- the gather of a paged KV history through a block table.
 * ``forward``   -- drives the above over every sequence and head of a layout.
+* ``backward``  -- dQ, dK, dV: the chain rule of the forward map, per
+                   sequence and head.
 
 Parity status: every function here is pinned by CPU tests against values the
 pages print, closed forms, library special cases, independent constructions
 and invariants (see tests/test_oracle_*.py).  No function is unpinned.
 """
 
-from . import masks, tiles, attention, paged, forward  # noqa: F401
+from . import masks, tiles, attention, paged, forward, backward  # noqa: F401

@@ -87,3 +87,31 @@ def layout_tiles(layout, BM: int, BN: int):
         full_idx[r, :full_cnt[r]] = full[r]
         part_idx[r, :part_cnt[r]] = part[r]
     return cls, full_cnt, part_cnt, full_idx, part_idx
+
+
+def layout_tile_columns(layout, BM: int, BN: int):
+    """The same classes read by kv-tile column: for column ``s * n_kt + b``
+    the ascending FULL and PARTIAL query-tile indices a of tiles (a, b) of
+    sequence s -- the orientation a pass that owns one kv tile and visits the
+    query tiles that see it needs (the xorl issue's transposed block-sparse
+    metadata for the backward, section "Verified FA4 gaps").  Returns
+    (full_cnt, part_cnt [cols], full_idx, part_idx [cols, n_qt]) with unused
+    slots -1."""
+    cls = layout_tiles(layout, BM, BN)[0]
+    n_kt = cls.shape[1]
+    n_qt = cls.shape[0] // max(layout.n_seqs, 1)
+    cols = layout.n_seqs * n_kt
+    full_cnt = np.zeros(cols, np.int32)
+    part_cnt = np.zeros(cols, np.int32)
+    full_idx = np.full((cols, n_qt), -1, np.int32)
+    part_idx = np.full((cols, n_qt), -1, np.int32)
+    for s in range(layout.n_seqs):
+        block = cls[s * n_qt:(s + 1) * n_qt]  # [n_qt, n_kt] of sequence s
+        for b in range(n_kt):
+            c = s * n_kt + b
+            f = np.nonzero(block[:, b] == FULL)[0]
+            p = np.nonzero(block[:, b] == PARTIAL)[0]
+            full_cnt[c], part_cnt[c] = len(f), len(p)
+            full_idx[c, :len(f)] = f
+            part_idx[c, :len(p)] = p
+    return full_cnt, part_cnt, full_idx, part_idx

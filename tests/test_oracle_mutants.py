@@ -215,3 +215,53 @@ def test_mutant_loss_copy_misses_own_thinking(monkeypatch):
         return ((tk < tq) & ~away) | ((tk == tq) & (rq == history) & ~away) | \
                ((tk == tq) & (rq != history) & (rk != history) & ~((rq == loss) & (rk == think)))
     assert _dup_mutant(monkeypatch, wrong) >= 1
+
+
+import test_oracle_backward as tb
+from oracle import backward as obackward
+
+
+def _bwd_mutant(monkeypatch, fn):
+    monkeypatch.setattr(obackward, "sequence_backward", fn)
+    return _fails(tb.test_backward_matches_central_differences,
+                  tb.test_backward_matches_torch_autograd_float64)
+
+
+def test_mutant_backward_without_softmax_correction(monkeypatch):
+    def wrong(q, k, v, vis, scale, do):  # dS = P * dP, the row term dropped
+        p = obackward.probabilities(q, k, vis, scale)
+        ds = p * (do @ np.asarray(v).T)
+        return scale * ds @ k, scale * ds.T @ q, p.T @ do
+    assert _bwd_mutant(monkeypatch, wrong) >= 1
+
+
+def test_mutant_backward_missing_scale_on_dk(monkeypatch):
+    def wrong(q, k, v, vis, scale, do):
+        p = obackward.probabilities(q, k, vis, scale)
+        dp = do @ np.asarray(v).T
+        ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        return scale * ds @ k, ds.T @ q, p.T @ do
+    assert _bwd_mutant(monkeypatch, wrong) >= 1
+
+
+def test_mutant_backward_unnormalised_probabilities(monkeypatch):
+    def wrong(q, k, v, vis, scale, do):  # exp(S) without dividing by the row sum
+        s = np.where(vis, (np.asarray(q) @ np.asarray(k).T) * scale, -np.inf)
+        p = np.exp(s - np.where(vis.any(1), s.max(1, initial=-np.inf), 0)[:, None])
+        dp = do @ np.asarray(v).T
+        ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        return scale * ds @ k, scale * ds.T @ q, p.T @ do
+    assert _bwd_mutant(monkeypatch, wrong) >= 1
+
+
+def test_mutant_tile_columns_off_by_one(monkeypatch):
+    orig = tiles.layout_tile_columns
+
+    def wrong(layout, BM, BN):
+        fc, pc, fi, pi = orig(layout, BM, BN)
+        fi = np.where(fi >= 0, fi + 1, fi)  # query-tile index shifted
+        return fc, pc, fi, pi
+
+    monkeypatch.setattr(tiles, "layout_tile_columns", wrong)
+    assert _fails(tb.test_tile_columns_transpose_the_printed_diagram,
+                  lambda: tb.test_tile_columns_reexpand_to_the_classes("causal")) >= 1
