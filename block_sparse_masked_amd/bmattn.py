@@ -30,8 +30,9 @@ STATUS = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "EALIGN", 4: "EHIP", 5: "E
 
 EXPORTS = ("bmattn_block_mask_shape", "bmattn_build_block_mask", "bmattn_forward_workspace_size",
            "bmattn_forward", "bmattn_paged_gather", "bmattn_debug_dense_mask", "bmattn_validate",
-           "bmattn_duplicated_answer_ids", "bmattn_status_string", "bmattn_last_error",
-           "bmattn_abi_version")
+           "bmattn_duplicated_answer_ids", "bmattn_transpose_block_mask",
+           "bmattn_backward_workspace_size", "bmattn_backward", "bmattn_status_string",
+           "bmattn_last_error", "bmattn_abi_version")
 
 _p = ctypes.c_void_p
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -65,6 +66,28 @@ class FwdArgsC(ctypes.Structure):
                 ("block_table", _p), ("block_table_stride", ctypes.c_int64),
                 ("num_pages", ctypes.c_int64), ("scale", ctypes.c_float),
                 ("reserved0", ctypes.c_int32), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class BlockMaskColsC(ctypes.Structure):
+    _fields_ = [("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
+                ("n_seqs", ctypes.c_int32), ("n_qt", ctypes.c_int32), ("n_kt", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32),
+                ("full_cnt", _p), ("part_cnt", _p), ("full_idx", _p), ("part_idx", _p),
+                ("col_order", _p)]
+
+
+class BwdArgsC(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("reserved0", ctypes.c_int32)] + [
+        f for name in ("q", "k", "v", "o", "do")
+        for f in ((name if name != "do" else "dout", _p), (f"{name}_stride_tok", ctypes.c_int64),
+                  (f"{name}_stride_head", ctypes.c_int64))] + [
+        ("lse", _p), ("lse_stride_head", ctypes.c_int64)] + [
+        f for name in ("dq", "dk", "dv")
+        for f in ((name, _p), (f"{name}_stride_tok", ctypes.c_int64),
+                  (f"{name}_stride_head", ctypes.c_int64))] + [
+        ("scale", ctypes.c_float), ("reserved1", ctypes.c_int32), ("workspace", _p),
+        ("workspace_bytes", ctypes.c_size_t)]
 
 
 class BmattnError(RuntimeError):
@@ -107,6 +130,13 @@ def lib():
                                       ctypes.c_int64, _p, _p]
         L.bmattn_duplicated_answer_ids.argtypes = [ctypes.POINTER(MaskDescC), _p, ctypes.c_int32,
                                                    ctypes.c_int32, _p, _p, _p, _p]
+        L.bmattn_transpose_block_mask.argtypes = [ctypes.POINTER(BlockMaskC),
+                                                  ctypes.POINTER(BlockMaskColsC), _p]
+        L.bmattn_backward_workspace_size.argtypes = [ctypes.POINTER(BwdArgsC),
+                                                     ctypes.POINTER(MaskDescC),
+                                                     ctypes.POINTER(ctypes.c_size_t)]
+        L.bmattn_backward.argtypes = [ctypes.POINTER(BwdArgsC), ctypes.POINTER(MaskDescC),
+                                      ctypes.POINTER(BlockMaskC), ctypes.POINTER(BlockMaskColsC), _p]
         for name in EXPORTS:
             getattr(L, name).restype = getattr(L, name).restype or ctypes.c_int
         _LIB = L
@@ -331,6 +361,93 @@ def validate(desc: MaskDesc, block_table=None, page_size: int = 0, num_pages: in
                                  int(page_size), int(num_pages), _ptr(flags), _stream(stream)),
            "bmattn_validate")
     return int(flags.item())
+
+
+@dataclass
+class BlockMaskCols:
+    """Column lists of a block mask (see bmattn_block_mask_cols)."""
+
+    block_m: int
+    block_n: int
+    n_seqs: int
+    n_qt: int
+    n_kt: int
+    full_cnt: torch.Tensor
+    part_cnt: torch.Tensor
+    full_idx: torch.Tensor
+    part_idx: torch.Tensor
+    col_order: torch.Tensor
+
+    def c(self) -> BlockMaskColsC:
+        return BlockMaskColsC(self.block_m, self.block_n, self.n_seqs, self.n_qt, self.n_kt, 0,
+                              _ptr(self.full_cnt), _ptr(self.part_cnt), _ptr(self.full_idx),
+                              _ptr(self.part_idx), _ptr(self.col_order))
+
+
+def transpose_block_mask(tiles: BlockMask, out: Optional[BlockMaskCols] = None,
+                         stream=None) -> BlockMaskCols:
+    """bmattn_transpose_block_mask: the column (kv-tile major) lists."""
+    if out is None:
+        cols = tiles.n_seqs * tiles.n_kt
+        i32 = dict(dtype=torch.int32, device=tiles.tile_class.device)
+        out = BlockMaskCols(tiles.block_m, tiles.block_n, tiles.n_seqs, tiles.n_qt, tiles.n_kt,
+                            torch.empty(cols, **i32), torch.empty(cols, **i32),
+                            torch.empty(cols * tiles.n_qt, **i32), torch.empty(cols * tiles.n_qt, **i32),
+                            torch.empty(cols, **i32))
+    t, c = tiles.c(), out.c()
+    _check(lib().bmattn_transpose_block_mask(ctypes.byref(t), ctypes.byref(c), _stream(stream)),
+           "bmattn_transpose_block_mask")
+    return out
+
+
+BWD_ROWS = (128, 64)   # block mask of the dQ pass (the forward's)
+BWD_COLS = (64, 128)   # block mask whose column lists drive the dK / dV pass
+
+
+def build_backward_cols(desc: MaskDesc, tiles: Optional[BlockMask] = None,
+                        out: Optional[BlockMaskCols] = None, stream=None):
+    """The 64 x 128 block mask of ``desc`` and its column lists; returns
+    (tiles, cols).  Pass both back to rebuild into the same arrays."""
+    tiles = build_block_mask(desc, *BWD_COLS, out=tiles, stream=stream)
+    return tiles, transpose_block_mask(tiles, out=out, stream=stream)
+
+
+def _bwd_args(q, k, v, o, do, lse, dq, dk, dv, scale=0.0, workspace=None):
+    H, D = q.shape[-2], q.shape[-1]
+    return BwdArgsC(_dtype_code(q.dtype), H, D, 0,
+                    _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1),
+                    _ptr(v), v.stride(0), v.stride(1), _ptr(o), o.stride(0), o.stride(1),
+                    _ptr(do), do.stride(0), do.stride(1), _ptr(lse), lse.stride(0) if lse is not None else 0,
+                    _ptr(dq), dq.stride(0), dq.stride(1), _ptr(dk), dk.stride(0), dk.stride(1),
+                    _ptr(dv), dv.stride(0), dv.stride(1), float(scale), 0, _ptr(workspace),
+                    0 if workspace is None else workspace.numel() * workspace.element_size())
+
+
+def backward_workspace_size(q, desc: MaskDesc) -> int:
+    a = _bwd_args(q, q, q, q, q, None, q, q, q)
+    n = ctypes.c_size_t()
+    d = desc.c()
+    _check(lib().bmattn_backward_workspace_size(ctypes.byref(a), ctypes.byref(d), ctypes.byref(n)),
+           "bmattn_backward_workspace_size")
+    return n.value
+
+
+def backward(q, k, v, o, lse, do, desc: MaskDesc, rows: BlockMask, cols: BlockMaskCols, *,
+             scale: float = 0.0, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """bmattn_backward: (dQ, dK, dV) like q, k, v.  ``rows`` is the forward's
+    128 x 64 block mask, ``cols`` the column lists of the 64 x 128 one
+    (build_backward_cols)."""
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        need = backward_workspace_size(q, desc)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    a = _bwd_args(q, k, v, o, do, lse, dq, dk, dv, scale, workspace)
+    d, t, c = desc.c(), rows.c(), cols.c()
+    _check(lib().bmattn_backward(ctypes.byref(a), ctypes.byref(d), ctypes.byref(t), ctypes.byref(c),
+                                 _stream(stream)), "bmattn_backward")
+    return dq, dk, dv
 
 
 def duplicated_answer_ids(desc: MaskDesc, role_q: torch.Tensor, *, loss_role: int = 2,

@@ -22,7 +22,7 @@ LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libbmattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "mask_kernels.hip", "forward_prefill.hip", "forward_prefill_bf16.hip",
+SOURCES = ["api.hip", "mask_kernels.hip", "forward_prefill.hip", "forward_prefill_bf16.hip", "backward_bf16.hip",
            "forward_decode.hip"]
 
 FLAGS = [

@@ -185,6 +185,74 @@ int check_fwd(const bmattn_fwd_args* a, const bmattn_mask_desc* d, const bmattn_
   return BMATTN_OK;
 }
 
+int check_cols(const bmattn_block_mask* t, const bmattn_block_mask_cols* c) {
+  if (c == nullptr) return fail(BMATTN_EINVAL, "column lists are NULL");
+  if (c->block_m != t->block_m || c->block_n != t->block_n || c->n_seqs != t->n_seqs ||
+      c->n_qt != t->n_qt || c->n_kt != t->n_kt)
+    return fail(BMATTN_EINVAL,
+                "column lists shape (%dx%d, n_seqs %d, n_qt %d, n_kt %d) does not match the block "
+                "mask (%dx%d, n_seqs %d, n_qt %d, n_kt %d)",
+                c->block_m, c->block_n, c->n_seqs, c->n_qt, c->n_kt, t->block_m, t->block_n,
+                t->n_seqs, t->n_qt, t->n_kt);
+  if (c->full_cnt == nullptr || c->part_cnt == nullptr || c->full_idx == nullptr ||
+      c->part_idx == nullptr || c->col_order == nullptr)
+    return fail(BMATTN_EINVAL, "column list array is NULL");
+  return BMATTN_OK;
+}
+
+ColsDev cols_dev(const bmattn_block_mask_cols* c) {
+  ColsDev x{};
+  x.n_seqs = c->n_seqs;
+  x.n_qt = c->n_qt;
+  x.n_kt = c->n_kt;
+  x.full_cnt = c->full_cnt;
+  x.part_cnt = c->part_cnt;
+  x.full_idx = c->full_idx;
+  x.part_idx = c->part_idx;
+  x.col_order = c->col_order;
+  return x;
+}
+
+size_t bwd_workspace(const bmattn_bwd_args* a, const bmattn_mask_desc* d) {
+  return (size_t)(2 * (int64_t)a->num_heads * d->total_q) * sizeof(float);
+}
+
+// dtype, head_dim and head count (all the workspace size depends on).
+int check_bwd_shape(const bmattn_bwd_args* a, const bmattn_mask_desc* d) {
+  if (a == nullptr) return fail(BMATTN_EINVAL, "backward arguments are NULL");
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (a->dtype != BMATTN_BF16)
+    return fail(BMATTN_EUNSUPPORTED, "the backward is compiled for BF16 only (got dtype %d)", a->dtype);
+  if (a->head_dim != 64 && a->head_dim != 128)
+    return fail(BMATTN_EUNSUPPORTED, "head_dim %d is not compiled (64 or 128)", a->head_dim);
+  if (a->num_heads < 1) return fail(BMATTN_EINVAL, "num_heads must be >= 1");
+  return BMATTN_OK;
+}
+
+int check_bwd(const bmattn_bwd_args* a, const bmattn_mask_desc* d) {
+  int rc = check_bwd_shape(a, d);
+  if (rc) return rc;
+  const void* ptrs[9] = {a->q, a->k, a->v, a->o, a->dout, a->dq, a->dk, a->dv, a->lse};
+  for (const void* x : ptrs)
+    if (x == nullptr) return fail(BMATTN_EINVAL, "q, k, v, o, dout, lse, dq, dk and dv must be non-NULL");
+  for (int i = 0; i < 8; ++i)
+    if (!aligned16(ptrs[i])) return fail(BMATTN_EALIGN, "q, k, v, o, dout, dq, dk and dv must be 16-byte aligned");
+  const int64_t strides[16] = {a->q_stride_tok,  a->q_stride_head,  a->k_stride_tok,  a->k_stride_head,
+                               a->v_stride_tok,  a->v_stride_head,  a->o_stride_tok,  a->o_stride_head,
+                               a->do_stride_tok, a->do_stride_head, a->dq_stride_tok, a->dq_stride_head,
+                               a->dk_stride_tok, a->dk_stride_head, a->dv_stride_tok, a->dv_stride_head};
+  for (int i = 0; i < 16; ++i) {
+    if (strides[i] < 0) return fail(BMATTN_EINVAL, "negative stride");
+    if ((strides[i] * 2) % 16 != 0)
+      return fail(BMATTN_EALIGN, "token/head strides must be multiples of 16 bytes");
+  }
+  if (a->lse_stride_head < d->total_q) return fail(BMATTN_EINVAL, "lse_stride_head must be >= total_q");
+  if (!(std::isfinite(a->scale)) || a->scale < 0.f)
+    return fail(BMATTN_EINVAL, "scale must be finite and >= 0 (0 selects 1/sqrt(head_dim))");
+  return BMATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -292,6 +360,121 @@ int bmattn_forward(const bmattn_fwd_args* a, const bmattn_mask_desc* desc,
     e = launch_forward_prefill(p, a->dtype, paged, st);
   }
   if (e != hipSuccess) return hip_fail(e, "bmattn_forward launch");
+  return BMATTN_OK;
+}
+
+int bmattn_transpose_block_mask(const bmattn_block_mask* tiles, const bmattn_block_mask_cols* out,
+                                void* stream) {
+  if (tiles == nullptr) return fail(BMATTN_EINVAL, "block mask is NULL");
+  if (tiles->tile_class == nullptr) return fail(BMATTN_EINVAL, "tile_class is NULL");
+  if (tiles->n_seqs < 1 || tiles->n_qt < 1 || tiles->n_kt < 1)
+    return fail(BMATTN_EINVAL, "block mask shape must be positive");
+  int rc = check_cols(tiles, out);
+  if (rc) return rc;
+  if (out->full_cnt == nullptr) return fail(BMATTN_EINVAL, "column list array is NULL");
+  TilesDev t{};
+  t.block_m = tiles->block_m;
+  t.block_n = tiles->block_n;
+  t.n_seqs = tiles->n_seqs;
+  t.n_qt = tiles->n_qt;
+  t.n_kt = tiles->n_kt;
+  t.tile_class = tiles->tile_class;
+  hipError_t e = launch_transpose_block_mask(t, cols_dev(out), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bmattn_transpose_block_mask launch");
+  return BMATTN_OK;
+}
+
+int bmattn_backward_workspace_size(const bmattn_bwd_args* args, const bmattn_mask_desc* desc,
+                                   size_t* bytes) {
+  if (bytes == nullptr) return fail(BMATTN_EINVAL, "bytes is NULL");
+  int rc = check_bwd_shape(args, desc);
+  if (rc) return rc;
+  *bytes = bwd_workspace(args, desc);
+  return BMATTN_OK;
+}
+
+int bmattn_backward(const bmattn_bwd_args* a, const bmattn_mask_desc* desc,
+                    const bmattn_block_mask* rows, const bmattn_block_mask_cols* cols,
+                    void* stream) {
+  int rc = check_bwd(a, desc);
+  if (rc) return rc;
+  rc = check_tiles(desc, rows, false);
+  if (rc) return rc;
+  if (rows->block_m != 128 || rows->block_n != 64)
+    return fail(BMATTN_EUNSUPPORTED, "rows must be a 128x64 block mask (got %dx%d)", rows->block_m,
+                rows->block_n);
+  if (cols == nullptr) return fail(BMATTN_EINVAL, "column lists are NULL");
+  if (cols->block_m != 64 || cols->block_n != 128)
+    return fail(BMATTN_EUNSUPPORTED, "cols must come from a 64x128 block mask (got %dx%d)",
+                cols->block_m, cols->block_n);
+  int32_t cq, ck;
+  int64_t crows, ctiles;
+  rc = shape(desc, 64, 128, &cq, &ck, &crows, &ctiles);
+  if (rc) return rc;
+  if (cols->n_seqs != desc->n_seqs || cols->n_qt != cq || cols->n_kt != ck)
+    return fail(BMATTN_EINVAL, "column lists shape does not match the description");
+  if (cols->full_cnt == nullptr || cols->part_cnt == nullptr || cols->full_idx == nullptr ||
+      cols->part_idx == nullptr || cols->col_order == nullptr)
+    return fail(BMATTN_EINVAL, "column list array is NULL");
+  const size_t need = bwd_workspace(a, desc);
+  if (need > 0 && (a->workspace == nullptr || a->workspace_bytes < need))
+    return fail(BMATTN_EWORKSPACE, "the backward needs a workspace of %zu bytes (got %zu)", need,
+                a->workspace == nullptr ? (size_t)0 : a->workspace_bytes);
+  if (need > 0 && !aligned16(a->workspace)) return fail(BMATTN_EALIGN, "workspace must be 16-byte aligned");
+  BwdDev p{};
+  p.mask = to_dev(desc);
+  p.max_lq = desc->max_seqlen_q;
+  p.max_lk = desc->max_seqlen_k;
+  p.n_qt = rows->n_qt;
+  p.n_kt = rows->n_kt;
+  p.full_cnt = rows->full_cnt;
+  p.part_cnt = rows->part_cnt;
+  p.full_idx = rows->full_idx;
+  p.part_idx = rows->part_idx;
+  p.row_order = rows->row_order;
+  p.c_n_qt = cols->n_qt;
+  p.c_n_kt = cols->n_kt;
+  p.c_full_cnt = cols->full_cnt;
+  p.c_part_cnt = cols->part_cnt;
+  p.c_full_idx = cols->full_idx;
+  p.c_part_idx = cols->part_idx;
+  p.col_order = cols->col_order;
+  p.num_heads = a->num_heads;
+  p.head_dim = a->head_dim;
+  p.q = a->q;
+  p.k = a->k;
+  p.v = a->v;
+  p.o = a->o;
+  p.dout = a->dout;
+  p.dq = a->dq;
+  p.dk = a->dk;
+  p.dv = a->dv;
+  p.lse = a->lse;
+  p.q_st = a->q_stride_tok;
+  p.q_sh = a->q_stride_head;
+  p.k_st = a->k_stride_tok;
+  p.k_sh = a->k_stride_head;
+  p.v_st = a->v_stride_tok;
+  p.v_sh = a->v_stride_head;
+  p.o_st = a->o_stride_tok;
+  p.o_sh = a->o_stride_head;
+  p.do_st = a->do_stride_tok;
+  p.do_sh = a->do_stride_head;
+  p.dq_st = a->dq_stride_tok;
+  p.dq_sh = a->dq_stride_head;
+  p.dk_st = a->dk_stride_tok;
+  p.dk_sh = a->dk_stride_head;
+  p.dv_st = a->dv_stride_tok;
+  p.dv_sh = a->dv_stride_head;
+  p.lse_sh = a->lse_stride_head;
+  const float scale = a->scale > 0.f ? a->scale : 1.0f / std::sqrt((float)a->head_dim);
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  float* ws = static_cast<float*>(a->workspace);
+  p.ws_di = ws;
+  p.ws_l2 = ws == nullptr ? nullptr : ws + (int64_t)a->num_heads * desc->total_q;
+  hipError_t e = launch_backward_bf16(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "bmattn_backward launch");
   return BMATTN_OK;
 }
 

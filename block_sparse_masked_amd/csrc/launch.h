@@ -50,7 +50,56 @@ struct FwdDev {
   int32_t n_splits;      // splits per row
 };
 
+// Column lists of a block mask (kv-tile major): for column s * n_kt + b the
+// ascending FULL / PARTIAL query-tile indices of tiles (a, b) of sequence s.
+struct ColsDev {
+  int32_t n_seqs, n_qt, n_kt;
+  int32_t* full_cnt;   // [n_seqs * n_kt]
+  int32_t* part_cnt;
+  int32_t* full_idx;   // [n_seqs * n_kt * n_qt]
+  int32_t* part_idx;
+  int32_t* col_order;  // [n_seqs * n_kt]
+};
+
+// Backward parameters: the forward's row lists (query tiles of 128, kv tiles
+// of 64) for the dQ pass and the column lists of a 64 x 128 block mask for
+// the dK / dV pass.
+struct BwdDev {
+  MaskDev mask;
+  int32_t max_lq, max_lk;
+  int32_t n_qt, n_kt;  // row tiling
+  const int32_t* full_cnt;
+  const int32_t* part_cnt;
+  const int32_t* full_idx;
+  const int32_t* part_idx;
+  const int32_t* row_order;
+  int32_t c_n_qt, c_n_kt;  // column tiling
+  const int32_t* c_full_cnt;
+  const int32_t* c_part_cnt;
+  const int32_t* c_full_idx;
+  const int32_t* c_part_idx;
+  const int32_t* col_order;
+  int32_t num_heads, head_dim;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  const float* lse;
+  int64_t q_st, q_sh, k_st, k_sh, v_st, v_sh, o_st, o_sh, do_st, do_sh;
+  int64_t dq_st, dq_sh, dk_st, dk_sh, dv_st, dv_sh, lse_sh;
+  float scale;       // softmax scale
+  float scale_log2;  // scale * log2(e)
+  float* ws_di;      // [H, total_q] rowsum(dO * O)
+  float* ws_l2;      // [H, total_q] LSE * log2(e) (0 where LSE = -inf)
+};
+
 hipError_t launch_build_block_mask(const MaskDev& m, const TilesDev& t, hipStream_t st);
+hipError_t launch_transpose_block_mask(const TilesDev& t, const ColsDev& c, hipStream_t st);
+hipError_t launch_backward_bf16(const BwdDev& p, hipStream_t st);
 hipError_t launch_debug_dense_mask(const MaskDev& m, const TilesDev& t, int seq, uint8_t* out,
                                    int64_t out_stride, hipStream_t st);
 hipError_t launch_validate(const MaskDev& m, int32_t max_lq, int32_t max_lk,

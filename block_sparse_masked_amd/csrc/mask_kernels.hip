@@ -243,6 +243,52 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(TilesDev t, int rows
   if (r < rows) t.row_order[rank] = r;
 }
 
+// Column lists: one workgroup per (sequence s, kv tile b) reads the classes
+// of tiles (a, b) down the column and compacts the FULL and PARTIAL query
+// tiles in ascending a with ballots, as the row lists are compacted.
+__global__ __launch_bounds__(kThreads) void transpose_kernel(TilesDev t, ColsDev c) {
+  __shared__ int32_t wave_tot[2][kThreads / 64];
+  const int col = blockIdx.x;
+  const int s = col / c.n_kt, b = col % c.n_kt;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t coloff = (int64_t)col * c.n_qt;
+  int full_base = 0, part_base = 0;
+  for (int a0 = 0; a0 < c.n_qt; a0 += kThreads) {
+    const int a = a0 + tid;
+    const uint8_t cls =
+        a < c.n_qt ? t.tile_class[((int64_t)s * c.n_qt + a) * c.n_kt + b] : (uint8_t)BMATTN_TILE_EMPTY;
+    const uint64_t fm = __ballot(cls == BMATTN_TILE_FULL);
+    const uint64_t pm = __ballot(cls == BMATTN_TILE_PARTIAL);
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int frank = __popcll(fm & lt), prank = __popcll(pm & lt);
+    if (lane == 0) {
+      wave_tot[0][wave] = __popcll(fm);
+      wave_tot[1][wave] = __popcll(pm);
+    }
+    __syncthreads();
+    int fo = full_base, po = part_base, ft = 0, pt = 0;
+    for (int w = 0; w < kThreads / 64; ++w) {
+      if (w < wave) {
+        fo += wave_tot[0][w];
+        po += wave_tot[1][w];
+      }
+      ft += wave_tot[0][w];
+      pt += wave_tot[1][w];
+    }
+    if (cls == BMATTN_TILE_FULL) c.full_idx[coloff + fo + frank] = a;
+    if (cls == BMATTN_TILE_PARTIAL) c.part_idx[coloff + po + prank] = a;
+    full_base += ft;
+    part_base += pt;
+    __syncthreads();
+  }
+  for (int i = full_base + tid; i < c.n_qt; i += kThreads) c.full_idx[coloff + i] = -1;
+  for (int i = part_base + tid; i < c.n_qt; i += kThreads) c.part_idx[coloff + i] = -1;
+  if (tid == 0) {
+    c.full_cnt[col] = full_base;
+    c.part_cnt[col] = part_base;
+  }
+}
+
 // Small FULL / CAUSAL problems in one workgroup.  Without ids, a row's
 // classes follow from the sequence bounds in closed form: the non-empty kv
 // tiles are j < ne, with ne = floor(kmax / BN) + 1 for the last visible key
@@ -475,6 +521,22 @@ hipError_t launch_build_block_mask(const MaskDev& m, const TilesDev& t, hipStrea
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(schedule_kernel, dim3((rows + kThreads - 1) / kThreads), dim3(kThreads), 0,
                      st, t, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_block_mask(const TilesDev& t, const ColsDev& c, hipStream_t st) {
+  const int cols = c.n_seqs * c.n_kt;
+  if (cols == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_kernel, dim3(cols), dim3(kThreads), 0, st, t, c);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // The schedule of the columns: the row ranking over the column counts.
+  TilesDev v = t;
+  v.full_cnt = c.full_cnt;
+  v.part_cnt = c.part_cnt;
+  v.row_order = c.col_order;
+  hipLaunchKernelGGL(schedule_kernel, dim3((cols + kThreads - 1) / kThreads), dim3(kThreads), 0, st,
+                     v, cols);
   return hipGetLastError();
 }
 

@@ -205,6 +205,86 @@ int bmattn_forward_workspace_size(const bmattn_fwd_args* args, const bmattn_mask
 int bmattn_forward(const bmattn_fwd_args* args, const bmattn_mask_desc* desc,
                    const bmattn_block_mask* tiles, void* stream);
 
+/* ---- column lists (kv-tile major) -------------------------------------------
+ * The classes of a block mask read by kv-tile column: for column
+ * c = s * n_kt + b, the ascending indices a of the FULL tiles (a, b) of
+ * sequence s in full_idx[c * n_qt + 0 .. full_cnt[c] - 1], the PARTIAL ones
+ * likewise (unused slots -1), and col_order: the columns by descending
+ * listed-tile count, ties by ascending column.  This is the transposed
+ * orientation a backward pass that owns one kv tile needs [XORL "Verified
+ * FA4 gaps": the missing transposed backward metadata].  All arrays are
+ * caller-allocated device memory. */
+typedef struct {
+  int32_t block_m, block_n;
+  int32_t n_seqs, n_qt, n_kt;
+  int32_t reserved0;
+  int32_t* full_cnt;   /* [n_seqs * n_kt]                                     */
+  int32_t* part_cnt;   /* [n_seqs * n_kt]                                     */
+  int32_t* full_idx;   /* [n_seqs * n_kt * n_qt]                              */
+  int32_t* part_idx;   /* [n_seqs * n_kt * n_qt]                              */
+  int32_t* col_order;  /* [n_seqs * n_kt]                                     */
+} bmattn_block_mask_cols;
+
+/* Writes the column lists of a built block mask (reads tiles->tile_class
+ * only).  out's block_m, block_n, n_seqs, n_qt and n_kt must equal tiles'.
+ * Bit-exact. */
+int bmattn_transpose_block_mask(const bmattn_block_mask* tiles, const bmattn_block_mask_cols* out,
+                                void* stream);
+
+/* ---- backward ----------------------------------------------------------------
+ * Gradients of the forward above for an upstream gradient dO: with
+ * P = exp(S * scale - LSE) recomputed from the forward's LSE,
+ *   dV = P^T dO,  dP = dO V^T,  dS = P (dP - rowsum(dO * O)),
+ *   dQ = scale dS K,  dK = scale dS^T Q
+ * (the chain rule of [TFP21 21.1] with the mask of [TFP21 21.2; TFP9 9.2];
+ * the pages print no backward formulas).  Only listed tiles are visited:
+ * dK and dV by kv tile over the column lists of a block mask with tiles of
+ * 64 x 128 (cols; see bmattn_transpose_block_mask), dQ by query tile over
+ * the forward's block mask with tiles of 128 x 64 (rows).  No atomics: each
+ * output element has one writer and a fixed summation order, so the result
+ * is bit-reproducible run to run and does not depend on the other sequences
+ * of the batch [XORL "Determinism" and "Batch / packing invariance"].
+ *
+ * Compiled: dtype BF16 (inputs and gradients), head_dim 64 or 128,
+ * contiguous K/V (no block table).  Layouts as the forward: Q, O, dO, dQ
+ * [total_q, H, D]; K, V, dK, dV [total_k, H, D], head_dim contiguous, token
+ * and head strides in elements (multiples of 8); LSE fp32 [H, total_q] with
+ * lse_stride_head, as the forward wrote it.  dQ, dK and dV are overwritten
+ * (keys that no query sees get 0).  The workspace holds two fp32 arrays of
+ * H * total_q (bmattn_backward_workspace_size).
+ */
+typedef struct {
+  int32_t dtype;          /* bmattn_dtype; BF16 only                          */
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t reserved0;
+  const void* q;    int64_t q_stride_tok, q_stride_head;
+  const void* k;    int64_t k_stride_tok, k_stride_head;
+  const void* v;    int64_t v_stride_tok, v_stride_head;
+  const void* o;    int64_t o_stride_tok, o_stride_head;
+  const void* dout; int64_t do_stride_tok, do_stride_head;
+  const float* lse; int64_t lse_stride_head;
+  void* dq;         int64_t dq_stride_tok, dq_stride_head;
+  void* dk;         int64_t dk_stride_tok, dk_stride_head;
+  void* dv;         int64_t dv_stride_tok, dv_stride_head;
+  float scale;            /* 0 -> 1/sqrt(head_dim); must match the forward's  */
+  int32_t reserved1;
+  void* workspace;        /* device scratch                                   */
+  size_t workspace_bytes;
+} bmattn_bwd_args;
+
+/* Bytes of workspace bmattn_backward needs (host only; reads dtype,
+ * num_heads and head_dim of args and the description's total_q). */
+int bmattn_backward_workspace_size(const bmattn_bwd_args* args, const bmattn_mask_desc* desc,
+                                   size_t* bytes);
+
+/* rows: built from desc with block_m 128, block_n 64 (the forward's).  cols:
+ * the column lists of a block mask built from desc with block_m 64,
+ * block_n 128. */
+int bmattn_backward(const bmattn_bwd_args* args, const bmattn_mask_desc* desc,
+                    const bmattn_block_mask* rows, const bmattn_block_mask_cols* cols,
+                    void* stream);
+
 /* ---- test and support exports ---------------------------------------------
  * Gathers the paged history of every sequence into out [total_k, H, D]
  * (contiguous, the pool's dtype) through the forward's own paged addressing

@@ -203,3 +203,37 @@ def test_missing_library_fails_loudly_on_first_call(tmp_path, monkeypatch):
     monkeypatch.setattr(bmattn, "_LIB", None)
     with pytest.raises(ImportError):
         bmattn.lib()
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    # The binding's ctypes structs have the header's sizes and offsets
+    # (compiled with the host C compiler; no device code involved).
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    checks = {
+        "bmattn_mask_desc": (bm.MaskDescC, ["kind", "think_role", "cu_seqlens_q", "turn_k"]),
+        "bmattn_block_mask": (bm.BlockMaskC, ["block_m", "tile_class", "row_order"]),
+        "bmattn_block_mask_cols": (bm.BlockMaskColsC, ["block_m", "full_cnt", "col_order"]),
+        "bmattn_fwd_args": (bm.FwdArgsC, ["q", "lse", "block_table", "scale", "workspace_bytes"]),
+        "bmattn_bwd_args": (bm.BwdArgsC, ["q", "dout", "do_stride_head", "lse", "dq", "dv_stride_head",
+                                          "scale", "workspace", "workspace_bytes"]),
+    }
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "bmattn.h"', 'int main(void) {']
+    for cname, (_, fields) in checks.items():
+        lines.append(f'  printf("{cname} %zu\\n", sizeof({cname}));')
+        for f in fields:
+            lines.append(f'  printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ['  return 0;', '}']
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = dict(l.split() for l in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                 text=True).stdout.splitlines())
+    for cname, (cls, fields) in checks.items():
+        assert int(out[cname]) == ctypes.sizeof(cls), cname
+        for f in fields:
+            assert int(out[f"{cname}.{f}"]) == getattr(cls, f).offset, (cname, f)
