@@ -33,7 +33,8 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 KERNEL_SOURCES = {"prefill": "block_sparse_masked_amd/csrc/forward_prefill_bf16.hip",
-                  "decode": "block_sparse_masked_amd/csrc/forward_decode.hip"}
+                  "decode": "block_sparse_masked_amd/csrc/forward_decode.hip",
+                  "backward": "block_sparse_masked_amd/csrc/backward_bf16.hip"}
 
 
 def visible_pairs(lay) -> int:
@@ -150,6 +151,120 @@ def cpu_baseline(lay, q, k, v, kp, vp, bt, flops_total: float, budget_s: float =
             "sample": f"the whole workload x{passes} (float64 numpy), {dt:.1f} s"}
 
 
+def cpu_baseline_backward(lay, q, k, v, do, flops_per_head: float, budget_s: float = 10.0):
+    """The oracle backward on the host cores, one head per pass (bounded)."""
+    from threadpoolctl import threadpool_info
+    from oracle import backward as obackward
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    qc, kc, vc, dc = q.cpu(), k.cpu(), v.cpu(), do.cpu()
+    passes, t0 = 0, time.perf_counter()
+    for h in range(lay.num_heads):
+        obackward.backward(lay, qc, kc, vc, dc, heads=[h])
+        passes += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops_per_head * passes / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{passes} of {lay.num_heads} heads (float64 numpy), {dt:.1f} s"}
+
+
+def bench_backward(args, lay, q, k, v, desc, tiles, torch, bm):
+    """The backward of the workload: flops = 10 * head_dim per visible pair
+    per head (S recomputed, dP, dV, dQ, dK: five products of 2 * head_dim,
+    the usual count of 2.5 forwards), inputs and the forward's O / LSE
+    resident in HBM."""
+    import synth
+    if lay.paged or lay.dtype != "bf16":
+        print("[bench] the backward is compiled for bf16 with contiguous K/V", file=sys.stderr)
+        sys.exit(2)
+    H, D = lay.num_heads, lay.head_dim
+    do = synth.make_dense_qkv(lay, seed=args.seed + 1000, device="cuda")[0]
+    o, lse = bm.forward(q, k, v, desc, tiles)
+    ctiles, cols = bm.build_backward_cols(desc)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(bm.backward_workspace_size(q, desc), 16), dtype=torch.uint8, device="cuda")
+
+    def step():
+        bm.build_backward_cols(desc, tiles=ctiles, out=cols)
+        bm.backward(q, k, v, o, lse, do, desc, tiles, cols, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    graph_steps = 1
+    if args.launch == "graph":
+        graph_steps = max(d for d in range(1, 21) if args.steps % d == 0)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(graph_steps):
+                step()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps // graph_steps):
+            graph.replay()
+    else:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # The backward call alone (prep, dK/dV and dQ kernels), HIP events on its stream.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record()
+        bm.backward(q, k, v, o, lse, do, desc, tiles, cols, dq=dq, dk=dk, dv=dv, workspace=ws)
+        b.record()
+    torch.cuda.synchronize()
+    bwd_ms = [a.elapsed_time(b) for a, b in evs]
+    bwd_avg = sum(bwd_ms) / len(bwd_ms)
+    fe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for a, b in fe:
+        a.record()
+        bm.forward(q, k, v, desc, tiles, out=o, lse=lse)
+        b.record()
+    torch.cuda.synchronize()
+    fwd_avg = sum(a.elapsed_time(b) for a, b in fe) / len(fe)
+
+    pairs = visible_pairs(lay)
+    flops = 10.0 * D * H * pairs
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (bwd_avg * 1e-3) / 1e12
+    res = {
+        "metric": "masked-attention backward TFLOP/s (unmasked FLOPs, 10*D per visible pair) "
+                  "+ % bf16 MFMA peak, 1 GPU",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": lay.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "pass": "backward", "seed": args.seed,
+                   "num_heads": H, "head_dim": D, "total_q": lay.total_q, "total_k": lay.total_k,
+                   "rows_tiles": list(bm.BWD_ROWS), "cols_tiles": list(bm.BWD_COLS),
+                   "launch": args.launch, "graph_steps": graph_steps, "visible_pairs_per_head": pairs,
+                   "flops_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic_from_profile("backward", args.workload)},
+        "detail": {"backward_call_ms": bwd_avg, "backward_call_ms_min": min(bwd_ms),
+                   "forward_call_ms": fwd_avg, "fwd_plus_bwd_ms": fwd_avg + bwd_avg},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle backward on the host cores", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline_backward(lay, q, k, v, do, flops / H, args.cpu_budget)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
 def copy_calibration(mib: int, steps: int):
     """A plain streaming kernel of known size: dst = src * 1 over fp32."""
     import torch
@@ -177,6 +292,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
                     help="replay each step as a captured HIP graph (default) or launch it eagerly")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward instead: a step is the column-list build of the "
+                         "backward's 64x128 block mask plus bmattn_backward (dQ, dK, dV)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the workload, run a plain fp32 copy of MIB MiB (read once, "
                          "written once) --steps times: the known-size kernel against which the "
@@ -217,6 +335,9 @@ def main():
             raise SystemExit(f"[bench] duplicated-answer layout check failed: {int(flags.item())}")
     BM, BN = (1, 64) if lay.max_q == 1 else (128, 64)
     tiles = bm.build_block_mask(desc, BM, BN)
+    if args.backward:
+        bench_backward(args, lay, q, k, v, desc, tiles, torch, bm)
+        return
     out = torch.empty_like(q)
     lse = torch.empty((H, lay.total_q), dtype=torch.float32, device=dev)
     ws_bytes = bm.forward_workspace_size(q, k, v, desc, tiles, block_table=bt)
