@@ -22,6 +22,11 @@ Sources:
   inference has once the thinking is stripped; later turns see the history
   copy only.
 * full -- no mask: Ch. 21, section 21.1's kernel before causal masking.
+* composed -- the xorl issue, section "Proposed work", item 3 (composable
+  builders: causal, document, shared-prefix and strip-thinking pieces) and
+  section "Current state in this tree" (causal + document + padding in one
+  mask): the AND of the chosen terms.  The document term keeps pairs of one
+  document; a negative document id marks padding, which no query sees.
 """
 
 from __future__ import annotations
@@ -34,9 +39,12 @@ def query_positions(Lq: int, Lk: int) -> np.ndarray:
     return np.arange(Lq, dtype=np.int64) + (Lk - Lq)
 
 
+TERMS = ("causal", "document", "shared_prefix", "strip_thinking")
+
+
 def visible(kind: str, Lq: int, Lk: int, *, seg_q=None, seg_k=None, role_q=None, role_k=None,
             turn_q=None, turn_k=None, think_role: int = 1, loss_role: int = 2,
-            history_role: int = 3) -> np.ndarray:
+            history_role: int = 3, doc_q=None, doc_k=None, terms=()) -> np.ndarray:
     """Dense boolean mask ``[Lq, Lk]`` for one sequence.
 
     ``seg_q``/``role_q``/``turn_q`` are per query row, ``seg_k``/``role_k``/
@@ -59,10 +67,39 @@ def visible(kind: str, Lq: int, Lk: int, *, seg_q=None, seg_k=None, role_q=None,
         rk = np.asarray(role_k, dtype=np.int64)[None, :]
         hidden = (rk == think_role) & (tk < tq)
         return causal & ~hidden
+    if kind == "composed":
+        return _composed(Lq, Lk, terms, causal, seg_q=seg_q, seg_k=seg_k, role_k=role_k,
+                         turn_q=turn_q, turn_k=turn_k, doc_q=doc_q, doc_k=doc_k,
+                         think_role=think_role)
     if kind == "strip_thinking_duplicated":
         return causal & _duplicated_answer_context(role_q, role_k, turn_q, turn_k,
                                                    think_role, loss_role, history_role)
     raise ValueError(f"unknown mask kind {kind!r}")
+
+
+def _composed(Lq, Lk, terms, causal, *, seg_q, seg_k, role_k, turn_q, turn_k, doc_q, doc_k,
+              think_role):
+    """AND of the chosen terms (any subset of TERMS, in any order)."""
+    unknown = set(terms) - set(TERMS)
+    if unknown:
+        raise ValueError(f"unknown mask terms {sorted(unknown)}")
+    vis = np.ones((Lq, Lk), dtype=bool)
+    if "causal" in terms:
+        vis &= causal
+    if "document" in terms:
+        dq = np.asarray(doc_q, dtype=np.int64)[:, None]
+        dk = np.asarray(doc_k, dtype=np.int64)[None, :]
+        vis &= (dk == dq) & (dk >= 0)
+    if "shared_prefix" in terms:
+        sq = np.asarray(seg_q, dtype=np.int64)[:, None]
+        sk = np.asarray(seg_k, dtype=np.int64)[None, :]
+        vis &= (sk == 0) | (sk == sq)
+    if "strip_thinking" in terms:
+        tq = np.asarray(turn_q, dtype=np.int64)[:, None]
+        tk = np.asarray(turn_k, dtype=np.int64)[None, :]
+        rk = np.asarray(role_k, dtype=np.int64)[None, :]
+        vis &= ~((rk == think_role) & (tk < tq))
+    return vis
 
 
 def _duplicated_answer_context(role_q, role_k, turn_q, turn_k, think_role, loss_role,
@@ -101,4 +138,5 @@ def visible_for_layout(layout, s: int) -> np.ndarray:
                    seg_q=ids.get("seg_q"), seg_k=ids.get("seg_k"), role_q=ids.get("role_q"),
                    role_k=ids.get("role_k"), turn_q=ids.get("turn_q"), turn_k=ids.get("turn_k"),
                    think_role=layout.think_role, loss_role=layout.loss_role,
-                   history_role=layout.history_role)
+                   history_role=layout.history_role, doc_q=ids.get("doc_q"),
+                   doc_k=ids.get("doc_k"), terms=layout.terms)

@@ -12,6 +12,7 @@ from .workloads import (  # noqa: F401
     LOSS_ROLE,
     HISTORY_ROLE,
     KINDS,
+    TERMS,
     Layout,
     causal_single,
     full_single,
@@ -19,6 +20,7 @@ from .workloads import (  # noqa: F401
     shared_prefix,
     strip_thinking,
     strip_thinking_duplicated,
+    shared_prefix_groups,
     paged_decode,
     config,
     CONFIG_NAMES,

@@ -11,7 +11,8 @@ Per-token ids describe structure only:
   * ``seg``  -- segment id (0 = shared prefix, i >= 1 = the i-th suffix),
   * ``role`` -- 0 user, 1 think, 2 answer; with duplicated answers 2 is the
     answer's loss copy and 3 its history copy,
-  * ``turn`` -- conversation turn index.
+  * ``turn`` -- conversation turn index,
+  * ``doc``  -- document index inside a packed sequence (negative: padding).
 
 Random values are float32 standard normals drawn from a torch generator on the
 requested device and rounded to the workload dtype (bf16 by round to nearest
@@ -30,7 +31,8 @@ USER_ROLE = 0
 THINK_ROLE = 1
 ANSWER_ROLE = LOSS_ROLE = 2
 HISTORY_ROLE = 3
-KINDS = ("full", "causal", "shared_prefix", "strip_thinking", "strip_thinking_duplicated")
+KINDS = ("full", "causal", "shared_prefix", "strip_thinking", "strip_thinking_duplicated", "composed")
+TERMS = ("causal", "document", "shared_prefix", "strip_thinking")
 
 
 def derive_seed(seed: int, *tags: int) -> int:
@@ -59,6 +61,9 @@ class Layout:
     role_k: Optional[np.ndarray] = None
     turn_q: Optional[np.ndarray] = None
     turn_k: Optional[np.ndarray] = None
+    doc_q: Optional[np.ndarray] = None
+    doc_k: Optional[np.ndarray] = None
+    terms: tuple = ()  # composed kind: the ANDed terms
     think_role: int = THINK_ROLE
     loss_role: int = LOSS_ROLE
     history_role: int = HISTORY_ROLE
@@ -109,11 +114,11 @@ class Layout:
         """The id slices that belong to sequence ``s`` (q-side and k-side)."""
         cq, ck = self.cu_q, self.cu_k
         out = {}
-        for name in ("seg_q", "role_q", "turn_q"):
+        for name in ("seg_q", "role_q", "turn_q", "doc_q"):
             a = getattr(self, name)
             if a is not None:
                 out[name] = a[cq[s]:cq[s + 1]]
-        for name in ("seg_k", "role_k", "turn_k"):
+        for name in ("seg_k", "role_k", "turn_k", "doc_k"):
             a = getattr(self, name)
             if a is not None:
                 out[name] = a[ck[s]:ck[s + 1]]
@@ -193,6 +198,30 @@ def strip_thinking_duplicated(n_turns: int = 8, user: int = 256, think: int = 15
                   notes={"n_turns": n_turns, "user": user, "think": think, "answer": answer})
 
 
+def shared_prefix_groups(n_groups: int = 4, prefix: int = 1024, n_suffix: int = 8,
+                         suffix: int = 384, pad: int = 256, H: int = 32, D: int = 128,
+                         dtype: str = "bf16") -> Layout:
+    """Several shared-prefix groups and trailing padding packed in ONE
+    sequence, told apart by document ids (composed: causal AND document AND
+    shared-prefix).  Group g is [P_g, S_g1, ..., S_gn] with document id g and
+    segment ids restarting per group (0 for P_g); padding has document -1."""
+    segs, docs = [], []
+    for g in range(n_groups):
+        seg = np.concatenate([np.zeros(prefix, np.int32)] +
+                             [np.full(suffix, i, np.int32) for i in range(1, n_suffix + 1)])
+        segs.append(seg)
+        docs.append(np.full(seg.size, g, np.int32))
+    segs.append(np.zeros(pad, np.int32))
+    docs.append(np.full(pad, -1, np.int32))
+    seg = np.concatenate(segs)
+    doc = np.concatenate(docs)
+    T = int(seg.size)
+    return Layout("shared_prefix_groups", "composed", dtype, H, D, [T], [T], seg_q=seg, seg_k=seg,
+                  doc_q=doc, doc_k=doc, terms=("causal", "document", "shared_prefix"),
+                  notes={"n_groups": n_groups, "prefix": prefix, "n_suffix": n_suffix,
+                         "suffix": suffix, "pad": pad})
+
+
 def paged_decode(seed: int = 0, n_seqs: int = 64, lo: int = 512, hi: int = 32768,
                  page_size: int = 16, H: int = 32, D: int = 128, dtype: str = "bf16") -> Layout:
     """One new query per sequence over a paged context of ragged length."""
@@ -203,7 +232,7 @@ def paged_decode(seed: int = 0, n_seqs: int = 64, lo: int = 512, hi: int = 32768
 
 
 CONFIG_NAMES = ("causal_f32", "packed_documents", "shared_prefix", "strip_thinking", "paged_decode",
-                "strip_thinking_duplicated")
+                "strip_thinking_duplicated", "shared_prefix_groups")
 
 
 def config(name: str, seed: int = 0) -> Layout:
@@ -220,6 +249,8 @@ def config(name: str, seed: int = 0) -> Layout:
         return paged_decode(seed)
     if name == "strip_thinking_duplicated":
         return strip_thinking_duplicated()
+    if name == "shared_prefix_groups":
+        return shared_prefix_groups()
     raise KeyError(name)
 
 
@@ -239,7 +270,8 @@ def random_layout(rng: np.random.Generator, kind: str, n_seqs: int = 3, max_len:
         lens_q = list(lens_k)
     else:
         lens_q = [min(decode_q, lk) for lk in lens_k]
-    seg_k = role_k = turn_k = seg_q = turn_q = role_q = None
+    seg_k = role_k = turn_k = seg_q = turn_q = role_q = doc_k = doc_q = None
+    terms = ()
     if kind == "shared_prefix":
         parts = []
         for L in lens_k:
@@ -293,6 +325,44 @@ def random_layout(rng: np.random.Generator, kind: str, n_seqs: int = 3, max_len:
             tparts.append(turn)
         role_k = np.concatenate(rparts).astype(np.int32) if rparts else np.zeros(0, np.int32)
         turn_k = np.concatenate(tparts).astype(np.int32) if tparts else np.zeros(0, np.int32)
+    elif kind == "composed":
+        # a random non-empty subset of the terms, with every id array drawn:
+        # documents as runs (some padding, id -1), segments as runs with 0
+        # first inside each document, roles and turns as in strip_thinking
+        while not terms:
+            terms = tuple(t for t in TERMS if rng.random() < 0.6)
+        sp, rp, tp, dp = [], [], [], []
+        for L in lens_k:
+            doc = np.zeros(L, np.int32)
+            seg = np.zeros(L, np.int32)
+            role = np.zeros(L, np.int32)
+            turn = np.zeros(L, np.int32)
+            pos, d = 0, 0
+            while pos < L:
+                e = min(L, pos + int(rng.integers(1, max(2, L // 2 + 1))))
+                doc[pos:e] = -1 if rng.random() < 0.15 else d
+                cuts = np.sort(rng.integers(pos, e + 1, size=n_segments - 1))
+                bounds = np.concatenate([[pos], cuts, [e]])
+                for i in range(n_segments):
+                    seg[bounds[i]:bounds[i + 1]] = i
+                d += 1
+                pos = e
+            p2, t = 0, 0
+            while p2 < L:
+                for r in (0, THINK_ROLE, 2):
+                    n = int(rng.integers(1, max(2, L // (n_turns * 2) + 2)))
+                    role[p2:p2 + n] = r
+                    turn[p2:p2 + n] = t
+                    p2 += n
+                    if p2 >= L:
+                        break
+                t += 1
+            sp.append(seg)
+            rp.append(role)
+            tp.append(turn)
+            dp.append(doc)
+        cat = lambda parts: np.concatenate(parts).astype(np.int32) if parts else np.zeros(0, np.int32)
+        seg_k, role_k, turn_k, doc_k = cat(sp), cat(rp), cat(tp), cat(dp)
     # q-side ids: the last lens_q[s] key positions of each sequence.
     cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(int)
 
@@ -306,11 +376,12 @@ def random_layout(rng: np.random.Generator, kind: str, n_seqs: int = 3, max_len:
 
     seg_q = q_side(seg_k)
     turn_q = q_side(turn_k)
+    doc_q = q_side(doc_k)
     if kind == "strip_thinking_duplicated":
         role_q = q_side(role_k)
     return Layout(f"random_{kind}", kind, dtype, H, D, lens_q, lens_k,
                   seg_q=seg_q, seg_k=seg_k, role_q=role_q, role_k=role_k, turn_q=turn_q,
-                  turn_k=turn_k,
+                  turn_k=turn_k, doc_q=doc_q, doc_k=doc_k, terms=terms,
                   paged=paged, page_size=page_size)
 
 

@@ -284,3 +284,77 @@ def test_duplicated_answers_reproduce_inference_contexts():
             assert np.abs(_toy_network(emb[seq_a], vis_a, weights)[at] - gen[len(replayed):]).max() > 1e-6
             diverged += 1
     assert diverged >= 1
+
+
+def _composed(terms, T, **ids):
+    ids = {k: np.asarray(v).astype(np.int32) for k, v in ids.items()}
+    return masks.visible("composed", T, T, terms=terms, seg_q=ids.get("seg"), seg_k=ids.get("seg"),
+                         role_k=ids.get("role"), turn_q=ids.get("turn"), turn_k=ids.get("turn"),
+                         doc_q=ids.get("doc"), doc_k=ids.get("doc"), think_role=synth.THINK_ROLE)
+
+
+def test_composed_document_strip_thinking_hand_worked():
+    g = _golden.load("composed_document_strip_10x10.txt")
+    vis = _composed(("causal", "document", "strip_thinking"), 10, role=g["role"], turn=g["turn"],
+                    doc=g["doc"])
+    assert np.array_equal(vis, g["visible"].astype(bool))
+    # the order of the terms does not matter
+    vis2 = _composed(("strip_thinking", "causal", "document"), 10, role=g["role"], turn=g["turn"],
+                     doc=g["doc"])
+    assert np.array_equal(vis2, vis)
+
+
+def test_shared_prefix_groups_hand_worked():
+    g = _golden.load("shared_prefix_groups_9x9.txt")
+    lay = synth.shared_prefix_groups(n_groups=2, prefix=2, n_suffix=2, suffix=1, pad=1, H=1, D=8)
+    assert np.array_equal(lay.seg_k, g["seg"]) and np.array_equal(lay.doc_k, g["doc"])
+    assert np.array_equal(masks.visible_for_layout(lay, 0), g["visible"].astype(bool))
+
+
+def test_composed_single_terms_are_the_plain_kinds():
+    rng = np.random.default_rng(12)
+    for _ in range(5):
+        T = int(rng.integers(1, 40))
+        seg = np.sort(rng.integers(0, 3, T))
+        role = rng.integers(0, 3, T)
+        turn = np.sort(rng.integers(0, 4, T))
+        kw = dict(seg=seg, role=role, turn=turn)
+        assert np.array_equal(_composed(("causal",), T, **kw), masks.visible("causal", T, T))
+        assert np.array_equal(_composed(("causal", "shared_prefix"), T, **kw),
+                              masks.visible("shared_prefix", T, T, seg_q=seg, seg_k=seg))
+        assert np.array_equal(_composed(("causal", "strip_thinking"), T, **kw),
+                              masks.visible("strip_thinking", T, T, role_k=role, turn_q=turn,
+                                            turn_k=turn))
+        assert np.array_equal(_composed(("document",), T, doc=np.zeros(T)),
+                              masks.visible("full", T, T))
+
+
+def test_composed_document_term_equals_separate_sequences():
+    # Document ids inside one sequence give the block-diagonal of the
+    # documents' own masks; padding rows and columns are empty.
+    rng = np.random.default_rng(13)
+    for terms, kind in ((("causal", "document"), "causal"),
+                        (("causal", "document", "shared_prefix"), "shared_prefix"),
+                        (("causal", "document", "strip_thinking"), "strip_thinking")):
+        lens = rng.integers(1, 12, size=4)
+        pad = rng.random(4) < 0.3
+        doc = np.concatenate([np.full(n, -1 if p else d) for d, (n, p) in enumerate(zip(lens, pad))])
+        T = int(lens.sum())
+        seg = np.concatenate([np.sort(rng.integers(0, 3, n)) for n in lens])
+        role = rng.integers(0, 3, T)
+        turn = np.concatenate([np.sort(rng.integers(0, 3, n)) for n in lens])
+        expect = np.zeros((T, T), bool)
+        o = 0
+        for n, p in zip(lens, pad):
+            if not p:
+                sl = slice(o, o + n)
+                expect[sl, sl] = masks.visible(kind, n, n, seg_q=seg[sl], seg_k=seg[sl],
+                                               role_k=role[sl], turn_q=turn[sl], turn_k=turn[sl])
+            o += n
+        got = _composed(terms, T, seg=seg, role=role, turn=turn, doc=doc)
+        assert np.array_equal(got, expect), terms
+
+
+def test_composed_rejects_unknown_terms():
+    with pytest.raises(ValueError):
+        _composed(("causal", "sliding_window"), 3)

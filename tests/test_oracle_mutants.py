@@ -265,3 +265,36 @@ def test_mutant_tile_columns_off_by_one(monkeypatch):
     monkeypatch.setattr(tiles, "layout_tile_columns", wrong)
     assert _fails(tb.test_tile_columns_transpose_the_printed_diagram,
                   lambda: tb.test_tile_columns_reexpand_to_the_classes("causal")) >= 1
+
+
+def test_mutant_composed_padding_visible(monkeypatch):
+    orig = masks._composed
+
+    def wrong(Lq, Lk, terms, causal, **kw):  # negative document ids not treated as padding
+        kw = dict(kw)
+        if kw.get("doc_q") is not None:
+            kw["doc_q"] = np.abs(np.asarray(kw["doc_q"])) + 7
+            kw["doc_k"] = np.abs(np.asarray(kw["doc_k"])) + 7
+        return orig(Lq, Lk, terms, causal, **kw)
+
+    monkeypatch.setattr(masks, "_composed", wrong)
+    assert _fails(tm.test_composed_document_strip_thinking_hand_worked,
+                  tm.test_shared_prefix_groups_hand_worked,
+                  tm.test_composed_document_term_equals_separate_sequences) >= 1
+
+
+def test_mutant_composed_or_instead_of_and(monkeypatch):
+    orig = masks._composed
+
+    def wrong(Lq, Lk, terms, causal, **kw):  # terms ORed after the causal one
+        rest = [t for t in terms if t != "causal"]
+        vis = np.zeros((Lq, Lk), bool)
+        for t in rest:
+            vis |= orig(Lq, Lk, (t,), causal, **kw)
+        if not rest:
+            vis[:] = True
+        return vis & (causal if "causal" in terms else True)
+
+    monkeypatch.setattr(masks, "_composed", wrong)
+    assert _fails(tm.test_composed_document_strip_thinking_hand_worked,
+                  tm.test_shared_prefix_groups_hand_worked) >= 1
