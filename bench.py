@@ -12,7 +12,8 @@ The default workload is the packed-document batch (8 causal documents with
 lengths uniform in [64, 2048], 16 heads, head_dim 128, bf16).  Other named
 workloads: causal_f32, shared_prefix, strip_thinking, paged_decode,
 strip_thinking_duplicated (whose step starts with the relabelling of its ids,
-bmattn_duplicated_answer_ids).
+bmattn_duplicated_answer_ids), shared_prefix_groups (a composed mask: four
+shared-prefix groups and padding in one sequence).
 """
 
 from __future__ import annotations
@@ -51,6 +52,9 @@ def visible_pairs(lay) -> int:
             # a query at position p of turn t sees p + 1 keys minus t think spans
             tot += (T * (2 * b + T + 1)) // 2 - T * t * th
         return tot
+    if lay.name == "shared_prefix_groups":
+        g, P, n, S = (lay.notes[k] for k in ("n_groups", "prefix", "n_suffix", "suffix"))
+        return g * (P * (P + 1) // 2 + n * (S * P + S * (S + 1) // 2))  # padding sees nothing
     if lay.name == "strip_thinking_duplicated":
         u, th, a, n = (lay.notes[k] for k in ("user", "think", "answer", "n_turns"))
         tot = 0
@@ -127,7 +131,8 @@ def cpu_baseline(lay, q, k, v, kp, vp, bt, flops_total: float, budget_s: float =
                 "sample": f"{passes} of {lay.n_seqs} sequences x heads 0-3 (float64 numpy), {dt:.1f} s"}
     qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
     passes, t0 = 0, time.perf_counter()
-    if lay.name in ("shared_prefix", "strip_thinking", "strip_thinking_duplicated"):
+    if lay.name in ("shared_prefix", "strip_thinking", "strip_thinking_duplicated",
+                    "shared_prefix_groups"):
         # One head per pass of the single long sequence.
         import dataclasses
         one_head = dataclasses.replace(lay, num_heads=1)
@@ -327,7 +332,8 @@ def main():
                               seg_q=lay.seg_q, seg_k=lay.seg_k, role_q=lay.role_q,
                               role_k=lay.role_k, turn_q=lay.turn_q, turn_k=lay.turn_k,
                               think_role=lay.think_role, loss_role=lay.loss_role,
-                              history_role=lay.history_role)
+                              history_role=lay.history_role, doc_q=lay.doc_q, doc_k=lay.doc_k,
+                              terms=lay.terms)
     relabel = desc.duplicated_from is not None
     if relabel:
         flags = bm.relabel(desc, check=True)

@@ -21,9 +21,10 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libbmattn.so")
 
-MASK_FULL, MASK_CAUSAL, MASK_SHARED_PREFIX, MASK_STRIP_THINKING = 0, 1, 2, 3
+MASK_FULL, MASK_CAUSAL, MASK_SHARED_PREFIX, MASK_STRIP_THINKING, MASK_COMPOSED = 0, 1, 2, 3, 4
 KIND_CODES = {"full": MASK_FULL, "causal": MASK_CAUSAL, "shared_prefix": MASK_SHARED_PREFIX,
-              "strip_thinking": MASK_STRIP_THINKING}
+              "strip_thinking": MASK_STRIP_THINKING, "composed": MASK_COMPOSED}
+TERM_CODES = {"causal": 1, "document": 2, "shared_prefix": 4, "strip_thinking": 8}
 F32, BF16 = 0, 1
 TILE_EMPTY, TILE_PARTIAL, TILE_FULL = 0, 1, 2
 STATUS = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "EALIGN", 4: "EHIP", 5: "EWORKSPACE"}
@@ -42,9 +43,9 @@ class MaskDescC(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("n_seqs", ctypes.c_int32),
                 ("max_seqlen_q", ctypes.c_int32), ("max_seqlen_k", ctypes.c_int32),
                 ("total_q", ctypes.c_int64), ("total_k", ctypes.c_int64),
-                ("think_role", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("think_role", ctypes.c_int32), ("terms", ctypes.c_int32),
                 ("cu_seqlens_q", _p), ("cu_seqlens_k", _p), ("seg_q", _p), ("seg_k", _p),
-                ("role_k", _p), ("turn_q", _p), ("turn_k", _p)]
+                ("role_k", _p), ("turn_q", _p), ("turn_k", _p), ("doc_q", _p), ("doc_k", _p)]
 
 
 class BlockMaskC(ctypes.Structure):
@@ -186,16 +187,21 @@ class MaskDesc:
     # For a description relabelled from duplicated answers: (the description
     # with the layout's own ids, role_q, loss_role, history_role).
     duplicated_from: Optional[tuple] = None
+    terms: int = 0  # COMPOSED: OR of TERM_CODES
+    doc_q: Optional[torch.Tensor] = None
+    doc_k: Optional[torch.Tensor] = None
 
     @staticmethod
     def create(kind, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, *,
                device="cuda", seg_q=None, seg_k=None, role_q=None, role_k=None, turn_q=None,
                turn_k=None, think_role: int = 1, loss_role: int = 2,
-               history_role: int = 3) -> "MaskDesc":
+               history_role: int = 3, doc_q=None, doc_k=None, terms=()) -> "MaskDesc":
         """A description; kind "strip_thinking_duplicated" takes the ids of a
         layout with duplicated answer spans (role_q, role_k with loss_role
         and history_role, turn_q, turn_k) and returns the STRIP_THINKING
-        description that bmattn_duplicated_answer_ids relabels them to."""
+        description that bmattn_duplicated_answer_ids relabels them to; kind
+        "composed" takes ``terms`` (names of TERM_CODES, or their OR) and the
+        ids those terms read (document: doc_q, doc_k)."""
         if kind == "strip_thinking_duplicated":
             src = MaskDesc.create("strip_thinking", cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                                   max_seqlen_k, device=device, role_k=role_k, turn_q=turn_q,
@@ -208,15 +214,21 @@ class MaskDesc:
         n = int(cq.numel()) - 1
         tq = int(cq[-1].item()) if n >= 0 else 0
         tk = int(ck[-1].item()) if n >= 0 else 0
+        if kind == MASK_COMPOSED:
+            bits = terms if isinstance(terms, int) else sum(TERM_CODES[t] for t in set(terms))
+        else:
+            bits = 0
         return MaskDesc(kind, n, int(max_seqlen_q), int(max_seqlen_k), tq, tk, cq, ck,
                         _i32(seg_q, device), _i32(seg_k, device), _i32(role_k, device),
-                        _i32(turn_q, device), _i32(turn_k, device), int(think_role))
+                        _i32(turn_q, device), _i32(turn_k, device), int(think_role),
+                        terms=int(bits), doc_q=_i32(doc_q, device), doc_k=_i32(doc_k, device))
 
     def c(self) -> MaskDescC:
         return MaskDescC(self.kind, self.n_seqs, self.max_seqlen_q, self.max_seqlen_k,
-                         self.total_q, self.total_k, self.think_role, 0,
+                         self.total_q, self.total_k, self.think_role, self.terms,
                          _ptr(self.cu_seqlens_q), _ptr(self.cu_seqlens_k), _ptr(self.seg_q),
-                         _ptr(self.seg_k), _ptr(self.role_k), _ptr(self.turn_q), _ptr(self.turn_k))
+                         _ptr(self.seg_k), _ptr(self.role_k), _ptr(self.turn_q), _ptr(self.turn_k),
+                         _ptr(self.doc_q), _ptr(self.doc_k))
 
 
 @dataclass

@@ -41,7 +41,7 @@ constexpr int32_t kDecodeSplitTiles = 8;
 
 int check_desc(const bmattn_mask_desc* d) {
   if (d == nullptr) return fail(BMATTN_EINVAL, "mask description is NULL");
-  if (d->kind < BMATTN_MASK_FULL || d->kind > BMATTN_MASK_STRIP_THINKING)
+  if (d->kind < BMATTN_MASK_FULL || d->kind > BMATTN_MASK_COMPOSED)
     return fail(BMATTN_EINVAL, "unknown mask kind %d", d->kind);
   if (d->n_seqs < 1) return fail(BMATTN_EINVAL, "n_seqs must be >= 1 (got %d)", d->n_seqs);
   if (d->max_seqlen_q < 1 || d->max_seqlen_k < 1)
@@ -57,6 +57,20 @@ int check_desc(const bmattn_mask_desc* d) {
   if (d->kind == BMATTN_MASK_STRIP_THINKING &&
       (d->role_k == nullptr || d->turn_q == nullptr || d->turn_k == nullptr))
     return fail(BMATTN_EINVAL, "STRIP_THINKING needs role_k, turn_q and turn_k");
+  if (d->kind == BMATTN_MASK_COMPOSED) {
+    if (d->terms <= 0 || d->terms > 15)
+      return fail(BMATTN_EINVAL, "COMPOSED needs terms, a non-empty OR of BMATTN_TERM_* (got %d)",
+                  d->terms);
+    if ((d->terms & BMATTN_TERM_DOCUMENT) && (d->doc_q == nullptr || d->doc_k == nullptr))
+      return fail(BMATTN_EINVAL, "the DOCUMENT term needs doc_q and doc_k");
+    if ((d->terms & BMATTN_TERM_SHARED_PREFIX) && (d->seg_q == nullptr || d->seg_k == nullptr))
+      return fail(BMATTN_EINVAL, "the SHARED_PREFIX term needs seg_q and seg_k");
+    if ((d->terms & BMATTN_TERM_STRIP_THINKING) &&
+        (d->role_k == nullptr || d->turn_q == nullptr || d->turn_k == nullptr))
+      return fail(BMATTN_EINVAL, "the STRIP_THINKING term needs role_k, turn_q and turn_k");
+  } else if (d->terms != 0) {
+    return fail(BMATTN_EINVAL, "terms must be 0 unless the kind is COMPOSED (got %d)", d->terms);
+  }
   return BMATTN_OK;
 }
 
@@ -65,6 +79,13 @@ MaskDev to_dev(const bmattn_mask_desc* d) {
   m.kind = d->kind;
   m.n_seqs = d->n_seqs;
   m.think_role = d->think_role;
+  switch (d->kind) {
+    case BMATTN_MASK_FULL: m.terms = 0; break;
+    case BMATTN_MASK_CAUSAL: m.terms = BMATTN_TERM_CAUSAL; break;
+    case BMATTN_MASK_SHARED_PREFIX: m.terms = BMATTN_TERM_CAUSAL | BMATTN_TERM_SHARED_PREFIX; break;
+    case BMATTN_MASK_STRIP_THINKING: m.terms = BMATTN_TERM_CAUSAL | BMATTN_TERM_STRIP_THINKING; break;
+    default: m.terms = d->terms; break;
+  }
   m.total_q = d->total_q;
   m.total_k = d->total_k;
   m.cu_q = d->cu_seqlens_q;
@@ -74,6 +95,8 @@ MaskDev to_dev(const bmattn_mask_desc* d) {
   m.role_k = d->role_k;
   m.turn_q = d->turn_q;
   m.turn_k = d->turn_k;
+  m.doc_q = d->doc_q;
+  m.doc_k = d->doc_k;
   return m;
 }
 

@@ -65,8 +65,8 @@ struct Lay {
   static constexpr int kCh = kRowB / 16;                 // 16-byte columns per row
   static constexpr int kTileB = kTR * kRowB;             // bytes of one staged tile
   static constexpr int kT1 = kTileB;                     // second tile of a stage
-  static constexpr int kF = 2 * kTileB;                  // three float / int arrays of kTR
-  static constexpr int kStage = 2 * kTileB + 3 * kTR * 4;
+  static constexpr int kF = 2 * kTileB;                  // five float / int arrays of kTR
+  static constexpr int kStage = 2 * kTileB + 5 * kTR * 4;
   static constexpr int kCopies = kTileB / 1024 / kWaves; // 1 KiB copies per wave per tile
   static constexpr int kDT = D / 32;                     // 32-wide d blocks
   static_assert(kCopies >= 1 && kCopies * 1024 * kWaves == kTileB, "tile / copy mismatch");
@@ -161,23 +161,8 @@ __device__ __forceinline__ void copy_words(const void* base, int row0, int nrows
   copy4(static_cast<const char*>(base) + 4 * (int64_t)j, lds_addr(dst));
 }
 
-// Two 32-row score blocks of one wave against a staged tile: for block b,
-// acc_b = sum over 16-d steps of A(rows sigma, block b) * B[ks].
-template <int D>
-__device__ __forceinline__ void score_blocks(const char* T, const bf16x8 (&b)[D / 16], const Addr<D>& ad,
-                                             f32x16& s0, f32x16& s1) {
-  using L = Lay<D>;
-  s0 = f32x16{};
-  s1 = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(T + ad.a[ks]);
-    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(T + ad.a[ks] + 32 * L::kRowB);
-    s0 = mfma(a0, b[ks], s0);
-    s1 = mfma(a1, b[ks], s1);
-  }
-}
-
+// One 32-row score block of one wave against a staged tile: the sum over
+// 16-d steps of A(rows sigma of the block) * B[ks].
 template <int D>
 __device__ __forceinline__ f32x16 score_block(const char* T, const bf16x8 (&b)[D / 16], const Addr<D>& ad) {
   f32x16 s = f32x16{};
@@ -239,17 +224,40 @@ __device__ __forceinline__ void store_rows(void* dst, int64_t off_elems, const f
   }
 }
 
-// The element predicate with the kind read at run time (wave-uniform):
-// query row i (ids qid: segment or turn), key j (ids ka, kb: segment, or
-// role and turn).  Same condition as visible_k().
-__device__ __forceinline__ bool visible_rt(const MaskDev& m, const SeqBounds& b, int i, int32_t qid,
-                                           int j, int32_t ka, int32_t kb) {
+// The element predicate through the mask's terms (every kind is a set of
+// terms: m.terms), wave-uniform: query row i with ids q, key j with
+// segment, role, turn and document ids.  Same condition as visible_k().
+__device__ __forceinline__ bool visible_rt(const MaskDev& m, const SeqBounds& b, int i, QIds q,
+                                           int j, int32_t kseg, int32_t krole, int32_t kturn,
+                                           int32_t kdoc) {
   const bool in = (i < b.lq) & (j < b.lk);
-  const bool causal = (m.kind == BMATTN_MASK_FULL) | (j <= b.lk - b.lq + i);
-  const bool ids = m.kind == BMATTN_MASK_SHARED_PREFIX ? ((ka == 0) | (ka == qid))
-                   : m.kind == BMATTN_MASK_STRIP_THINKING ? !((ka == m.think_role) & (kb < qid))
-                                                         : true;
-  return in & causal & ids;
+  const bool causal = !(m.terms & BMATTN_TERM_CAUSAL) | (j <= b.lk - b.lq + i);
+  return in & causal & composed_ids_ok(m.terms, m.think_role, q, kseg, krole, kturn, kdoc);
+}
+
+// Key ids in term order (segment, role, turn, document) from load_kids().
+__device__ __forceinline__ KIds term_kids(const MaskDev& m, KIds k) {
+  if (m.kind == BMATTN_MASK_SHARED_PREFIX) return KIds{k.a, 0, 0, 0};
+  if (m.kind == BMATTN_MASK_STRIP_THINKING) return KIds{0, k.a, k.b, 0};
+  return k;
+}
+
+// The id arrays the terms read, by slot: keys 0 segment, 1 role, 2 turn,
+// 3 document; queries 0 segment, 1 turn, 2 document (nullptr: not read).
+__device__ __forceinline__ const int32_t* key_ids(const MaskDev& m, int slot) {
+  switch (slot) {
+    case 0: return (m.terms & BMATTN_TERM_SHARED_PREFIX) ? m.seg_k : nullptr;
+    case 1: return (m.terms & BMATTN_TERM_STRIP_THINKING) ? m.role_k : nullptr;
+    case 2: return (m.terms & BMATTN_TERM_STRIP_THINKING) ? m.turn_k : nullptr;
+    default: return (m.terms & BMATTN_TERM_DOCUMENT) ? m.doc_k : nullptr;
+  }
+}
+__device__ __forceinline__ const int32_t* query_ids(const MaskDev& m, int slot) {
+  switch (slot) {
+    case 0: return (m.terms & BMATTN_TERM_SHARED_PREFIX) ? m.seg_q : nullptr;
+    case 1: return (m.terms & BMATTN_TERM_STRIP_THINKING) ? m.turn_q : nullptr;
+    default: return (m.terms & BMATTN_TERM_DOCUMENT) ? m.doc_q : nullptr;
+  }
 }
 
 // ---- Di and LSE * log2(e) ---------------------------------------------------
@@ -303,7 +311,7 @@ __device__ __forceinline__ void dkdv_block(const char* stage, int qb, bool maske
   // Registers 8 c + e hold query q0 + 32 qb + 16 c + 8 g + e.
   const float* l2 = reinterpret_cast<const float*>(stage + L::kF);
   const float* di = l2 + kTR;
-  const int32_t* qid = reinterpret_cast<const int32_t*>(di + kTR);
+  const int32_t* qid = reinterpret_cast<const int32_t*>(di + kTR);  // segment, turn, document
   const float sl2 = p.scale_log2;
   bf16x8 pb[2], db[2];
 #pragma unroll
@@ -319,12 +327,19 @@ __device__ __forceinline__ void dkdv_block(const char* stage, int qb, bool maske
 #pragma unroll
     for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(s[8 * c + e], sl2, -lv[e]));
     if (masked) {
-      const int4 ia = *reinterpret_cast<const int4*>(qid + r0);
-      const int4 ib = *reinterpret_cast<const int4*>(qid + r0 + 4);
-      const int idv[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
+      int v[3][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pv[e] = visible_rt(p.mask, sb, q0 + r0 + e, idv[e], kj, kids.a, kids.b) ? pv[e] : 0.f;
+      for (int a = 0; a < 3; ++a) {
+        const int4 ia = *reinterpret_cast<const int4*>(qid + a * kTR + r0);
+        const int4 ib = *reinterpret_cast<const int4*>(qid + a * kTR + r0 + 4);
+        v[a][0] = ia.x; v[a][1] = ia.y; v[a][2] = ia.z; v[a][3] = ia.w;
+        v[a][4] = ib.x; v[a][5] = ib.y; v[a][6] = ib.z; v[a][7] = ib.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const QIds q{v[0][e], v[1][e], v[2][e]};
+        pv[e] = visible_rt(p.mask, sb, q0 + r0 + e, q, kj, kids.a, kids.b, kids.c, kids.d) ? pv[e] : 0.f;
+      }
     }
     float dsv[8];
 #pragma unroll
@@ -363,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdDev p) {
 
   const int kj = b * kRowTile + wave * 32 + l32;  // key of the lane inside the sequence
   const bool kvalid = kj < sb.lk;
-  const KIds kids = load_kids(p.mask, sb, kj);
+  const KIds kids = term_kids(p.mask, load_kids(p.mask, sb, kj));
   bf16x8 kf[D / 16], vf[D / 16];
   load_b_rows<D>(p.k, (sb.k0 + (kvalid ? kj : 0)) * p.k_st + (int64_t)h * p.k_sh, kvalid, g, kf);
   load_b_rows<D>(p.v, (sb.k0 + (kvalid ? kj : 0)) * p.v_st + (int64_t)h * p.v_sh, kvalid, g, vf);
@@ -379,9 +394,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdDev p) {
   const char* obase = static_cast<const char*>(p.dout) + (sb.q0 * p.do_st + (int64_t)h * p.do_sh) * 2;
   const float* l2base = p.ws_l2 + (int64_t)h * p.mask.total_q + sb.q0;
   const float* dibase = p.ws_di + (int64_t)h * p.mask.total_q + sb.q0;
-  const int32_t* qidbase = p.mask.kind == BMATTN_MASK_SHARED_PREFIX ? p.mask.seg_q + sb.q0
-                           : p.mask.kind == BMATTN_MASK_STRIP_THINKING ? p.mask.turn_q + sb.q0
-                                                                       : nullptr;
+  // Wave w stages query-id slot w (w < 3) of PARTIAL tiles.
+  const int32_t* qidsrc = wave < 3 ? query_ids(p.mask, wave) : nullptr;
+  const int32_t* qidbase = qidsrc != nullptr ? qidsrc + sb.q0 : nullptr;
   auto entry = [&](int t) -> int { return t < nfull ? flist[t] : plist[t - nfull]; };
   auto issue = [&](int t, char* stage) {
     const int a = entry(t);
@@ -390,7 +405,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdDev p) {
     copy_tile<D>(obase, p.do_st * 2, r0, sb.lq, wave, lane, stage + L::kT1);
     if (wave == 0) copy_words(l2base, r0, sb.lq, lane, stage + L::kF);
     if (wave == 1) copy_words(dibase, r0, sb.lq, lane, stage + L::kF + kTR * 4);
-    if (wave == 2 && qidbase != nullptr && t >= nfull) copy_words(qidbase, r0, sb.lq, lane, stage + L::kF + 2 * kTR * 4);
+    if (qidbase != nullptr && t >= nfull) copy_words(qidbase, r0, sb.lq, lane, stage + L::kF + (2 + wave) * kTR * 4);
   };
   if (ntiles > 0) issue(0, smem);
   end_of_tile();
@@ -418,10 +433,9 @@ template <int D>
 __device__ __forceinline__ void dq_tile(const char* stage, bool masked, const bf16x8 (&qf)[D / 16],
                                         const bf16x8 (&of)[D / 16], f32x16 (&dq)[D / 32],
                                         const Addr<D>& ad, const BwdDev& p, const SeqBounds& sb,
-                                        int k0, int qi, int32_t qid, float l2, float di, int g) {
+                                        int k0, int qi, QIds qids, float l2, float di, int g) {
   using L = Lay<D>;
-  const int32_t* ka = reinterpret_cast<const int32_t*>(stage + L::kF);
-  const int32_t* kb = ka + kTR;
+  const int32_t* kid = reinterpret_cast<const int32_t*>(stage + L::kF);  // segment, role, turn, document
   const float sl2 = p.scale_log2;
   // One 32-key block at a time: register r holds key k0 + 32 bl + 16 (r / 8)
   // + 8 g + r % 8.
@@ -439,15 +453,18 @@ __device__ __forceinline__ void dq_tile(const char* stage, bool masked, const bf
 #pragma unroll
       for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(fmaf(s[8 * c + e], sl2, -l2));
       if (masked) {
-        const int4 a0 = *reinterpret_cast<const int4*>(ka + j0);
-        const int4 a1 = *reinterpret_cast<const int4*>(ka + j0 + 4);
-        const int4 b0 = *reinterpret_cast<const int4*>(kb + j0);
-        const int4 b1 = *reinterpret_cast<const int4*>(kb + j0 + 4);
-        const int av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        const int bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        int v[4][8];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int4 x0 = *reinterpret_cast<const int4*>(kid + a * kTR + j0);
+          const int4 x1 = *reinterpret_cast<const int4*>(kid + a * kTR + j0 + 4);
+          v[a][0] = x0.x; v[a][1] = x0.y; v[a][2] = x0.z; v[a][3] = x0.w;
+          v[a][4] = x1.x; v[a][5] = x1.y; v[a][6] = x1.z; v[a][7] = x1.w;
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          pv[e] = visible_rt(p.mask, sb, qi, qid, k0 + j0 + e, av[e], bv[e]) ? pv[e] : 0.f;
+          pv[e] = visible_rt(p.mask, sb, qi, qids, k0 + j0 + e, v[0][e], v[1][e], v[2][e], v[3][e])
+                      ? pv[e] : 0.f;
       }
       float dsv[8];
 #pragma unroll
@@ -481,7 +498,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdDev p) {
   const int qi = a * kRowTile + wave * 32 + l32;
   const bool qvalid = qi < sb.lq;
   const QIds qids = load_qids(p.mask, sb, qi);
-  const int32_t qid = p.mask.kind == BMATTN_MASK_SHARED_PREFIX ? qids.seg : qids.turn;
   bf16x8 qf[D / 16], of[D / 16];
   load_b_rows<D>(p.q, (sb.q0 + (qvalid ? qi : 0)) * p.q_st + (int64_t)h * p.q_sh, qvalid, g, qf);
   load_b_rows<D>(p.dout, (sb.q0 + (qvalid ? qi : 0)) * p.do_st + (int64_t)h * p.do_sh, qvalid, g, of);
@@ -495,19 +511,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdDev p) {
 
   const char* kbase = static_cast<const char*>(p.k) + (sb.k0 * p.k_st + (int64_t)h * p.k_sh) * 2;
   const char* vbase = static_cast<const char*>(p.v) + (sb.k0 * p.v_st + (int64_t)h * p.v_sh) * 2;
-  const int32_t* ida = p.mask.kind == BMATTN_MASK_SHARED_PREFIX ? p.mask.seg_k + sb.k0
-                       : p.mask.kind == BMATTN_MASK_STRIP_THINKING ? p.mask.role_k + sb.k0
-                                                                   : nullptr;
-  const int32_t* idb = p.mask.kind == BMATTN_MASK_STRIP_THINKING ? p.mask.turn_k + sb.k0 : nullptr;
+  // Wave w stages key-id slot w of PARTIAL tiles.
+  const int32_t* kidsrc = key_ids(p.mask, wave);
+  const int32_t* kidbase = kidsrc != nullptr ? kidsrc + sb.k0 : nullptr;
   auto entry = [&](int t) -> int { return t < nfull ? flist[t] : plist[t - nfull]; };
   auto issue = [&](int t, char* stage) {
     const int r0 = entry(t) * kTR;
     copy_tile<D>(kbase, p.k_st * 2, r0, sb.lk, wave, lane, stage);
     copy_tile<D>(vbase, p.v_st * 2, r0, sb.lk, wave, lane, stage + L::kT1);
-    if (t >= nfull) {
-      if (wave == 0 && ida != nullptr) copy_words(ida, r0, sb.lk, lane, stage + L::kF);
-      if (wave == 1 && idb != nullptr) copy_words(idb, r0, sb.lk, lane, stage + L::kF + kTR * 4);
-    }
+    if (t >= nfull && kidbase != nullptr) copy_words(kidbase, r0, sb.lk, lane, stage + L::kF + wave * kTR * 4);
   };
   if (ntiles > 0) issue(0, smem);
   end_of_tile();
@@ -515,7 +527,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdDev p) {
     char* cur = smem + (t & 1) * L::kStage;
     if (t + 1 < ntiles) issue(t + 1, smem + ((t + 1) & 1) * L::kStage);
     const int k0 = entry(t) * kTR;
-    dq_tile<D>(cur, t >= nfull, qf, of, dq, ad, p, sb, k0, qi, qid, l2, di, g);
+    dq_tile<D>(cur, t >= nfull, qf, of, dq, ad, p, sb, k0, qi, qids, l2, di, g);
     end_of_tile();
   }
   if (qvalid) store_rows<D>(p.dq, (sb.q0 + qi) * p.dq_st + (int64_t)h * p.dq_sh, dq, p.scale, g);

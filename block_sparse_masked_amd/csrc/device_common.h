@@ -13,11 +13,14 @@
 namespace bmattn {
 
 // Mask description as the kernels see it (kernel-argument friendly copy).
+// `terms` holds the kind's predicate as BMATTN_TERM_* bits for every kind
+// (FULL: none; CAUSAL: causal; SHARED_PREFIX / STRIP_THINKING: causal and
+// the id term; COMPOSED: the description's terms), set by the host.
 struct MaskDev {
   int32_t kind;
   int32_t n_seqs;
   int32_t think_role;
-  int32_t pad0;
+  int32_t terms;
   int64_t total_q, total_k;
   const int32_t* cu_q;
   const int32_t* cu_k;
@@ -26,6 +29,8 @@ struct MaskDev {
   const int32_t* role_k;
   const int32_t* turn_q;
   const int32_t* turn_k;
+  const int32_t* doc_q;
+  const int32_t* doc_k;
 };
 
 // Bounds of one sequence, clamped so that every index derived from them lies
@@ -54,36 +59,58 @@ __device__ __forceinline__ SeqBounds seq_bounds(const MaskDev& m, int s, int32_t
   return b;
 }
 
-// Query-side ids of one query row (loaded once per row).
+// Query-side ids of one query row (loaded once per row); the ids the
+// kind's terms do not read stay 0.
 struct QIds {
-  int32_t seg, turn;
+  int32_t seg, turn, doc;
 };
 
 __device__ __forceinline__ QIds load_qids(const MaskDev& m, const SeqBounds& b, int i) {
-  QIds r{0, 0};
+  QIds r{0, 0, 0};
   if (i < b.lq) {
-    if (m.kind == BMATTN_MASK_SHARED_PREFIX) r.seg = m.seg_q[b.q0 + i];
-    if (m.kind == BMATTN_MASK_STRIP_THINKING) r.turn = m.turn_q[b.q0 + i];
+    if (m.terms & BMATTN_TERM_SHARED_PREFIX) r.seg = m.seg_q[b.q0 + i];
+    if (m.terms & BMATTN_TERM_STRIP_THINKING) r.turn = m.turn_q[b.q0 + i];
+    if (m.terms & BMATTN_TERM_DOCUMENT) r.doc = m.doc_q[b.q0 + i];
   }
   return r;
 }
 
-// Key-side ids of one key: the segment (shared-prefix) or the role and turn
-// (strip-thinking); unused fields are 0.
+// Key-side ids of one key.  Plain kinds: a = segment (shared-prefix) or
+// role (strip-thinking), b = turn (strip-thinking).  COMPOSED: a = segment,
+// b = role, c = turn, d = document.  Unread fields are 0.
 struct KIds {
-  int32_t a, b;
+  int32_t a, b, c, d;
 };
 
 __device__ __forceinline__ KIds load_kids(const MaskDev& m, const SeqBounds& b, int j) {
-  KIds r{0, 0};
+  KIds r{0, 0, 0, 0};
   if (j < b.lk) {
     if (m.kind == BMATTN_MASK_SHARED_PREFIX) r.a = m.seg_k[b.k0 + j];
     if (m.kind == BMATTN_MASK_STRIP_THINKING) {
       r.a = m.role_k[b.k0 + j];
       r.b = m.turn_k[b.k0 + j];
     }
+    if (m.kind == BMATTN_MASK_COMPOSED) {
+      if (m.terms & BMATTN_TERM_SHARED_PREFIX) r.a = m.seg_k[b.k0 + j];
+      if (m.terms & BMATTN_TERM_STRIP_THINKING) {
+        r.b = m.role_k[b.k0 + j];
+        r.c = m.turn_k[b.k0 + j];
+      }
+      if (m.terms & BMATTN_TERM_DOCUMENT) r.d = m.doc_k[b.k0 + j];
+    }
   }
   return r;
+}
+
+// The id terms of a COMPOSED mask for one pair (no causal, no bounds):
+// key ids in COMPOSED order (segment, role, turn, document).
+__device__ __forceinline__ bool composed_ids_ok(int32_t terms, int32_t think_role, QIds q,
+                                                int32_t kseg, int32_t krole, int32_t kturn,
+                                                int32_t kdoc) {
+  const bool doc = !(terms & BMATTN_TERM_DOCUMENT) | ((kdoc == q.doc) & (kdoc >= 0));
+  const bool pre = !(terms & BMATTN_TERM_SHARED_PREFIX) | (kseg == 0) | (kseg == q.seg);
+  const bool strip = !(terms & BMATTN_TERM_STRIP_THINKING) | !((krole == think_role) & (kturn < q.turn));
+  return doc & pre & strip;
 }
 
 // Element predicate: is key j of the sequence visible to its query row i?
@@ -98,7 +125,11 @@ __device__ __forceinline__ bool visible_k(const MaskDev& m, const SeqBounds& b, 
   const bool causal = in & (j <= b.lk - b.lq + i);
   if constexpr (KIND == BMATTN_MASK_CAUSAL) return causal;
   if constexpr (KIND == BMATTN_MASK_SHARED_PREFIX) return causal & ((kid.a == 0) | (kid.a == qi.seg));
-  return causal & !((kid.a == m.think_role) & (kid.b < qi.turn));  // STRIP_THINKING
+  if constexpr (KIND == BMATTN_MASK_STRIP_THINKING)
+    return causal & !((kid.a == m.think_role) & (kid.b < qi.turn));
+  // COMPOSED
+  const bool c = !(m.terms & BMATTN_TERM_CAUSAL) | (j <= b.lk - b.lq + i);
+  return in & c & composed_ids_ok(m.terms, m.think_role, qi, kid.a, kid.b, kid.c, kid.d);
 }
 
 __device__ __forceinline__ bool visible_ids(const MaskDev& m, const SeqBounds& b, int i, QIds qi,
@@ -107,7 +138,8 @@ __device__ __forceinline__ bool visible_ids(const MaskDev& m, const SeqBounds& b
     case BMATTN_MASK_FULL: return visible_k<BMATTN_MASK_FULL>(m, b, i, qi, j, kid);
     case BMATTN_MASK_CAUSAL: return visible_k<BMATTN_MASK_CAUSAL>(m, b, i, qi, j, kid);
     case BMATTN_MASK_SHARED_PREFIX: return visible_k<BMATTN_MASK_SHARED_PREFIX>(m, b, i, qi, j, kid);
-    default: return visible_k<BMATTN_MASK_STRIP_THINKING>(m, b, i, qi, j, kid);
+    case BMATTN_MASK_STRIP_THINKING: return visible_k<BMATTN_MASK_STRIP_THINKING>(m, b, i, qi, j, kid);
+    default: return visible_k<BMATTN_MASK_COMPOSED>(m, b, i, qi, j, kid);
   }
 }
 

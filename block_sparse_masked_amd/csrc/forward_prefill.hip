@@ -51,7 +51,7 @@ struct Cfg {
   static constexpr int kVP = kBN * kElem + 16;       // V^T row pitch in LDS (bytes)
   static constexpr int kKBuf = kBN * kKP;
   static constexpr int kVBuf = D * kVP;
-  static constexpr int kIdBuf = 2 * kBN * 4;              // key ids of a PARTIAL tile
+  static constexpr int kIdBuf = 4 * kBN * 4;              // key ids of a PARTIAL tile (KIds)
   static constexpr int kStage = kKBuf + kVBuf + kIdBuf;
   static constexpr int kKChunks = kBN * kCh / kThreads;  // K chunks per thread
   static constexpr int kKpt = kBN * kCh / kThreads;      // keys per thread (V staging)
@@ -194,6 +194,8 @@ struct Prefill {
       int32_t* ids = reinterpret_cast<int32_t*>(stage + C::kKBuf + C::kVBuf);
       ids[tid] = kid.a;
       ids[kBN + tid] = kid.b;
+      ids[2 * kBN + tid] = kid.c;
+      ids[3 * kBN + tid] = kid.d;
     }
     char* vt = stage + C::kKBuf;
     const int ch = tid % C::kCh, kg = tid / C::kCh;
@@ -298,9 +300,11 @@ __device__ __forceinline__ void mask_scores(float (&x)[32], const char* Ks, cons
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int jj = b * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
-      KIds kid{0, 0};
+      KIds kid{0, 0, 0, 0};
       if constexpr (KIND == BMATTN_MASK_SHARED_PREFIX || KIND == BMATTN_MASK_STRIP_THINKING)
-        kid = KIds{ids[jj], ids[kBN + jj]};
+        kid = KIds{ids[jj], ids[kBN + jj], 0, 0};
+      if constexpr (KIND == BMATTN_MASK_COMPOSED)
+        kid = KIds{ids[jj], ids[kBN + jj], ids[2 * kBN + jj], ids[3 * kBN + jj]};
       x[b * 16 + r] = visible_k<KIND>(p.mask, sb, qi, qids, kt * kBN + jj, kid) ? x[b * 16 + r]
                                                                                : -INFINITY;
     }
@@ -334,7 +338,10 @@ __device__ __forceinline__ void softmax_update(f32x16& s0, f32x16& s1, RowState<
       case BMATTN_MASK_SHARED_PREFIX:
         mask_scores<T, D, BMATTN_MASK_SHARED_PREFIX>(x, Ks, p, sb, kt, qi, qids, g);
         break;
-      default: mask_scores<T, D, BMATTN_MASK_STRIP_THINKING>(x, Ks, p, sb, kt, qi, qids, g); break;
+      case BMATTN_MASK_STRIP_THINKING:
+        mask_scores<T, D, BMATTN_MASK_STRIP_THINKING>(x, Ks, p, sb, kt, qi, qids, g);
+        break;
+      default: mask_scores<T, D, BMATTN_MASK_COMPOSED>(x, Ks, p, sb, kt, qi, qids, g); break;
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -543,7 +550,7 @@ __global__ __launch_bounds__(kThreads * KG, 2) void prefill_kernel(FwdDev p) {
 
   uint4 kr[C::kKChunks];
   uint4 vr[C::kKpt];
-  KIds kid{0, 0};
+  KIds kid{0, 0, 0, 0};
   const typename P::Offsets off = P::offsets(p, gtid);
   // The group's first tile is list entry grp.
   if (grp < ntiles) {

@@ -65,8 +65,8 @@ struct Lay {
   static constexpr int kCh = kRowB / 16;               // 16-byte columns per row
   static constexpr int kTileB = kBN * kRowB;           // bytes of a K (or V) tile
   static constexpr int kV = kTileB;                    // V tile offset in a stage
-  static constexpr int kIds = 2 * kTileB;              // key ids of a PARTIAL tile
-  static constexpr int kStage = 2 * kTileB + 2 * kBN * 4;
+  static constexpr int kIds = 2 * kTileB;              // key ids of a PARTIAL tile (4 arrays)
+  static constexpr int kStage = 2 * kTileB + 4 * kBN * 4;
   static constexpr int kCopies = kTileB / 1024 / kWaves;  // 1 KiB copies per wave per tile
   static constexpr int kDT = D / 32;                   // 32-wide output d tiles
   static_assert(kCopies >= 1 && kCopies * 1024 * kWaves == kTileB, "tile / copy mismatch");
@@ -118,13 +118,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
 }
 
+// The key-id array that wave gw stages for a PARTIAL tile, or none:
+// shared-prefix: the segment; strip-thinking: role, turn; composed: segment,
+// role, turn, document (those its terms read), one wave each.
+template <bool COMP>
+__device__ __forceinline__ const int32_t* id_source(const MaskDev& m, int gw) {
+  if constexpr (COMP) {
+    if (gw == 0) return (m.terms & BMATTN_TERM_SHARED_PREFIX) ? m.seg_k : nullptr;
+    if (gw == 1) return (m.terms & BMATTN_TERM_STRIP_THINKING) ? m.role_k : nullptr;
+    if (gw == 2) return (m.terms & BMATTN_TERM_STRIP_THINKING) ? m.turn_k : nullptr;
+    return (m.terms & BMATTN_TERM_DOCUMENT) ? m.doc_k : nullptr;
+  } else {
+    if (gw >= 2) return nullptr;
+    if (m.kind == BMATTN_MASK_SHARED_PREFIX) return gw == 0 ? m.seg_k : nullptr;
+    if (m.kind == BMATTN_MASK_STRIP_THINKING) return gw == 0 ? m.role_k : m.turn_k;
+    return nullptr;
+  }
+}
+
 // HBM -> LDS copies of one kv tile by one wave of the workgroup.  Copy u of wave
 // gw fills 16-byte slots [64 (gw*kCopies + u), +64) of the tile; slot s holds
 // row s / kCh, physical column s % kCh, i.e. logical column
 // (s % kCh) ^ swz(row).  Rows past the sequence end read its last row: those
 // keys are hidden by the predicate (they only occur in PARTIAL tiles), and
 // the values read are finite.
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool COMP>
 struct Copy {
   using L = Lay<D>;
   uint32_t koff[L::kCopies], voff[L::kCopies];
@@ -178,10 +196,7 @@ struct Copy {
   }
   __device__ __forceinline__ void ids(const FwdDev& p, const SeqBounds& sb, int kt, int gw, int lane,
                                       char* stage) const {
-    if (gw >= 2) return;
-    const int32_t* src = nullptr;
-    if (p.mask.kind == BMATTN_MASK_SHARED_PREFIX) src = gw == 0 ? p.mask.seg_k : nullptr;
-    if (p.mask.kind == BMATTN_MASK_STRIP_THINKING) src = gw == 0 ? p.mask.role_k : p.mask.turn_k;
+    const int32_t* src = id_source<COMP>(p.mask, gw);
     if (src != nullptr) {
       const int jj = max(min(kt * kBN + lane, sb.lk - 1), 0);
       copy4(src + sb.k0 + jj, lds_addr(stage + L::kIds + gw * kBN * 4));
@@ -199,15 +214,7 @@ struct Copy {
     } else {
       general(p, sb, s, h, kt, gw, lane, stage);
     }
-    if (masked && gw < 2) {
-      const int32_t* ids = nullptr;
-      if (p.mask.kind == BMATTN_MASK_SHARED_PREFIX) ids = gw == 0 ? p.mask.seg_k : nullptr;
-      if (p.mask.kind == BMATTN_MASK_STRIP_THINKING) ids = gw == 0 ? p.mask.role_k : p.mask.turn_k;
-      if (ids != nullptr) {
-        const int jj = max(min(kt * kBN + lane, sb.lk - 1), 0);
-        copy4(ids + sb.k0 + jj, lds_addr(stage + L::kIds + gw * kBN * 4));
-      }
-    }
+    if (masked) ids(p, sb, kt, gw, lane, stage);
   }
 };
 
@@ -298,7 +305,9 @@ template <int D, int KIND>
 __device__ __forceinline__ uint32_t visible_bits(const char* kstage, const FwdDev& p,
                                                  const SeqBounds& sb, int kt, int qi, QIds qids,
                                                  int g) {
-  const int lim = (KIND == BMATTN_MASK_FULL) ? sb.lk - 1 : min(sb.lk - 1, sb.lk - sb.lq + qi);
+  const bool causal = (KIND == BMATTN_MASK_COMPOSED) ? (p.mask.terms & BMATTN_TERM_CAUSAL) != 0
+                                                    : KIND != BMATTN_MASK_FULL;
+  const int lim = causal ? min(sb.lk - 1, sb.lk - sb.lq + qi) : sb.lk - 1;
   const int n = lim - kt * kBN - 8 * g + 1;  // keys 16 c + e < n are visible
   const int count = n <= 0 ? 0 : min(32, 8 * (n >> 4) + min(n & 15, 8));
   uint32_t bits = qi < sb.lq ? (count >= 32 ? 0xffffffffu : ((1u << count) - 1u)) : 0u;
@@ -326,6 +335,29 @@ __device__ __forceinline__ uint32_t visible_bits(const char* kstage, const FwdDe
     }
     bits &= keep;
   }
+  if constexpr (KIND == BMATTN_MASK_COMPOSED) {
+    // The four staged arrays: segment, role, turn, document (an array the
+    // terms do not read holds stale values that composed_ids_ok ignores).
+    const int32_t* ida = reinterpret_cast<const int32_t*>(kstage + Lay<D>::kIds);
+    uint32_t keep = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j0 = 16 * c + 8 * g;
+      int v[4][8];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int4 x0 = *reinterpret_cast<const int4*>(ida + a * kBN + j0);
+        const int4 x1 = *reinterpret_cast<const int4*>(ida + a * kBN + j0 + 4);
+        v[a][0] = x0.x; v[a][1] = x0.y; v[a][2] = x0.z; v[a][3] = x0.w;
+        v[a][4] = x1.x; v[a][5] = x1.y; v[a][6] = x1.z; v[a][7] = x1.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        keep |= (uint32_t)composed_ids_ok(p.mask.terms, p.mask.think_role, qids, v[0][e], v[1][e],
+                                          v[2][e], v[3][e]) << (8 * c + e);
+    }
+    bits &= keep;
+  }
   return bits;
 }
 
@@ -334,14 +366,16 @@ __device__ __forceinline__ uint32_t visible_bits(const char* kstage, const FwdDe
 // Register r of block b holds key kt*64 + b*32 + 16*(r/8) + 8*g + r%8.
 // Scores stay unscaled until the exponent: max(s * c) = c * max(s) for the
 // positive scale c, and exp2(s * c - m) is one fma and one exp.
-template <int D, bool MASKED>
+template <int D, bool MASKED, bool COMP>
 __device__ __forceinline__ void softmax_update(f32x16& s0, f32x16& s1, bf16x8 (&pf)[4], RowState<D>& st,
                                                const char* stage, const FwdDev& p,
                                                const SeqBounds& sb, int kt, int qi, QIds qids,
                                                int g) {
   if constexpr (MASKED) {
     uint32_t vis;
-    switch (p.mask.kind) {
+    if constexpr (COMP) {
+      vis = visible_bits<D, BMATTN_MASK_COMPOSED>(stage, p, sb, kt, qi, qids, g);
+    } else switch (p.mask.kind) {
       case BMATTN_MASK_FULL: vis = visible_bits<D, BMATTN_MASK_FULL>(stage, p, sb, kt, qi, qids, g); break;
       case BMATTN_MASK_CAUSAL: vis = visible_bits<D, BMATTN_MASK_CAUSAL>(stage, p, sb, kt, qi, qids, g); break;
       case BMATTN_MASK_SHARED_PREFIX:
@@ -434,12 +468,12 @@ __device__ __forceinline__ void pv_product(const char* stage, const bf16x8 (&pf)
 
 // One kv tile for one wave: copies of the next tile into `nxt`,
 // then the S product, softmax and P V product of tile kt from `cur`.
-template <int D, bool PAGED, bool MASKED>
+template <int D, bool PAGED, bool MASKED, bool COMP>
 __device__ __forceinline__ void kv_step(const char* cur, char* nxt, bool has_next, bool mnext,
                                         int ktn, int kt, const int32_t* ahead, int& kt_ahead,
                                         const FwdDev& p, const SeqBounds& sb,
                                         int s, int h, int gw, int lane, const bf16x8 (&q)[D / 16],
-                                        const Addr<D>& ad, const Copy<D, PAGED>& cp,
+                                        const Addr<D>& ad, const Copy<D, PAGED, COMP>& cp,
                                         RowState<D>& st, int qi, QIds qids, int g) {
   using L = Lay<D>;
   const bool whole = has_next && cp.whole(sb, ktn);
@@ -462,7 +496,7 @@ __device__ __forceinline__ void kv_step(const char* cur, char* nxt, bool has_nex
   if (whole) s_product<D, true>(cur, q, ad, s0, s1, tc);
   else s_product<D, false>(cur, q, ad, s0, s1, tc);
   bf16x8 pf[4];
-  softmax_update<D, MASKED>(s0, s1, pf, st, cur, p, sb, kt, qi, qids, g);
+  softmax_update<D, MASKED, COMP>(s0, s1, pf, st, cur, p, sb, kt, qi, qids, g);
   pv_product<D>(cur, pf, st, ad);
 }
 
@@ -485,7 +519,8 @@ __device__ __forceinline__ void end_of_tile() {
 // walks the row's kv-tile list with a double-buffered LDS stage.  Two
 // workgroups share a CU (66 KiB of LDS each) and synchronise independently,
 // so one workgroup's softmax runs beside the other's matrix work.
-template <int D, bool PAGED>
+// COMP: the COMPOSED kind (its predicate only); otherwise the four plain kinds.
+template <int D, bool PAGED, bool COMP>
 __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(FwdDev p) {
   using L = Lay<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * L::kStage];
@@ -539,7 +574,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(FwdDev p) {
   st.m = -INFINITY;
   st.l = 0.f;
   const Addr<D> ad(lane);
-  const Copy<D, PAGED> cp(p, wave, lane);
+  const Copy<D, PAGED, COMP> cp(p, wave, lane);
 
   // List entry t (FULL entries first, then PARTIAL ones), or none.
   auto entry_ptr = [&](int t) -> const int32_t* {
@@ -562,7 +597,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(FwdDev p) {
     const bool has_next = t + 1 < ntiles;
     const bool mnext = t + 1 >= nfull;
     int kt_ahead;
-    kv_step<D, PAGED, false>(smem + (t & 1) * L::kStage, smem + ((t + 1) & 1) * L::kStage, has_next,
+    kv_step<D, PAGED, false, COMP>(smem + (t & 1) * L::kStage, smem + ((t + 1) & 1) * L::kStage, has_next,
                              mnext, kt_nxt, kt_cur, entry_ptr(t + 2), kt_ahead, p, sb, s, h, wave,
                              lane, q, ad, cp, st, qi, qids, g);
     end_of_tile();
@@ -571,7 +606,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(FwdDev p) {
   }
   for (; t < ntiles; ++t) {
     int kt_ahead;
-    kv_step<D, PAGED, true>(smem + (t & 1) * L::kStage, smem + ((t + 1) & 1) * L::kStage,
+    kv_step<D, PAGED, true, COMP>(smem + (t & 1) * L::kStage, smem + ((t + 1) & 1) * L::kStage,
                             t + 1 < ntiles, true, kt_nxt, kt_cur, entry_ptr(t + 2), kt_ahead, p, sb,
                             s, h, wave, lane, q, ad, cp, st, qi, qids, g);
     end_of_tile();
@@ -607,10 +642,15 @@ hipError_t launch_d(const FwdDev& p, bool paged, hipStream_t st) {
   const uint32_t n_rows = (uint32_t)p.mask.n_seqs * p.n_qt;
   const uint32_t grid = n_rows * (uint32_t)p.num_heads;
   if (grid == 0) return hipSuccess;
-  if (paged) {
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, true>), dim3(grid), dim3(kThreads), 0, st, p);
+  const bool comp = p.mask.kind == BMATTN_MASK_COMPOSED;
+  if (paged && comp) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true>), dim3(grid), dim3(kThreads), 0, st, p);
+  } else if (paged) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, true, false>), dim3(grid), dim3(kThreads), 0, st, p);
+  } else if (comp) {
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, false, true>), dim3(grid), dim3(kThreads), 0, st, p);
   } else {
-    hipLaunchKernelGGL((prefill_bf16_kernel<D, false>), dim3(grid), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, false, false>), dim3(grid), dim3(kThreads), 0, st, p);
   }
   return hipGetLastError();
 }

@@ -123,6 +123,50 @@ __device__ uint8_t classify_tile(const MaskDev& m, const SeqBounds& b, int qlo, 
   return any_hid ? BMATTN_TILE_PARTIAL : BMATTN_TILE_FULL;
 }
 
+// COMPOSED masks: q ids of the tile's rows in qs / qt / qd (segment, turn,
+// document); `uniform` when every row of the tile that lies in the
+// sequence carries the ids q0.  Then a key is visible to all of them or to
+// none apart from the causal term, and the tiles that the causal term does
+// not cut follow from "every key" / "any key"; other tiles enumerate their
+// pairs until they see a visible and a hidden one.
+__device__ uint8_t classify_tile_composed(const MaskDev& m, const SeqBounds& b, int qlo, int klo,
+                                          int BM, int BN, bool uniform, QIds q0,
+                                          const int32_t* qs, const int32_t* qt, const int32_t* qd) {
+  if (qlo >= b.lq || klo >= b.lk) return BMATTN_TILE_EMPTY;
+  const int qhi = min(qlo + BM, b.lq);
+  const int khi = min(klo + BN, b.lk);
+  const bool inside = (qlo + BM <= b.lq) && (klo + BN <= b.lk);
+  const bool causal = (m.terms & BMATTN_TERM_CAUSAL) != 0;
+  const int64_t off = (int64_t)b.lk - b.lq;
+  if (causal && (int64_t)klo > (int64_t)(qhi - 1) + off) return BMATTN_TILE_EMPTY;
+  const bool causal_full = !causal || ((int64_t)klo + BN - 1 <= (int64_t)qlo + off);
+  if (uniform && causal_full) {
+    bool all = true, any = false;
+    for (int j = klo; j < khi; ++j) {
+      const KIds k = load_kids(m, b, j);
+      const bool ok = composed_ids_ok(m.terms, m.think_role, q0, k.a, k.b, k.c, k.d);
+      all &= ok;
+      any |= ok;
+    }
+    if (!any) return BMATTN_TILE_EMPTY;
+    return (all && inside) ? BMATTN_TILE_FULL : BMATTN_TILE_PARTIAL;
+  }
+  bool any_vis = false, any_hid = !inside;
+  for (int j = klo; j < khi; ++j) {
+    const KIds k = load_kids(m, b, j);
+    for (int i = qlo; i < qhi; ++i) {
+      const QIds q{qs[i - qlo], qt[i - qlo], qd[i - qlo]};
+      const bool v = (!causal || (int64_t)j <= off + i) &&
+                     composed_ids_ok(m.terms, m.think_role, q, k.a, k.b, k.c, k.d);
+      any_vis |= v;
+      any_hid |= !v;
+      if (any_vis && any_hid) return BMATTN_TILE_PARTIAL;
+    }
+  }
+  if (!any_vis) return BMATTN_TILE_EMPTY;
+  return any_hid ? BMATTN_TILE_PARTIAL : BMATTN_TILE_FULL;
+}
+
 // One workgroup per query-tile row: classifies the row's kv tiles in chunks
 // of 256 and appends FULL / PARTIAL indices in ascending order.
 // Staged key ids per chunk: tiles of BN keys, each run padded to BN + 1
@@ -131,6 +175,7 @@ constexpr int kKidKeys = 16384;
 
 __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev t) {
   __shared__ int32_t qid[kMaxBlock];
+  __shared__ int32_t qturn[kMaxBlock], qdoc[kMaxBlock];  // COMPOSED only
   __shared__ int32_t kid[kKidKeys + kThreads];
   __shared__ int32_t wave_tot[2][kThreads / 64];
   __shared__ int32_t red[2][kThreads / 64];
@@ -141,12 +186,20 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev 
   const SeqBounds b = seq_bounds(m, s, t.max_lq, t.max_lk);
   const int qlo = a * BM;
 
+  const bool composed = m.kind == BMATTN_MASK_COMPOSED;
+  const QIds q0 = load_qids(m, b, qlo);
+  int same = 1;
   // Row ids (segment for shared-prefix, turn for strip-thinking) and range.
   int32_t lmin = INT32_MAX, lmax = INT32_MIN;
   for (int i = tid; i < BM; i += kThreads) {
     QIds x = load_qids(m, b, qlo + i);
-    int32_t v = (m.kind == BMATTN_MASK_SHARED_PREFIX) ? x.seg : x.turn;
+    int32_t v = (m.kind == BMATTN_MASK_SHARED_PREFIX || composed) ? x.seg : x.turn;
     qid[i] = v;
+    if (composed) {
+      qturn[i] = x.turn;
+      qdoc[i] = x.doc;
+      if (qlo + i < b.lq) same &= (x.seg == q0.seg) & (x.turn == q0.turn) & (x.doc == q0.doc);
+    }
     if (qlo + i < b.lq) {
       lmin = min(lmin, v);
       lmax = max(lmax, v);
@@ -167,6 +220,9 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev 
     qmax = max(qmax, red[1][w]);
   }
 
+  // COMPOSED: do all the row's queries carry the ids of its first one?
+  const bool uniform = __syncthreads_and(same) != 0;
+
   const int64_t rowoff = (int64_t)row * t.n_kt;
   int full_base = 0, part_base = 0;
   // Chunks of tpc kv tiles, one per thread; for the id-based kinds the ids of
@@ -186,7 +242,8 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev 
     }
     uint8_t cls = BMATTN_TILE_EMPTY;
     if (tid < tpc && bidx < t.n_kt) {
-      cls = classify_tile(m, b, qlo, bidx * BN, BM, BN, qid, qmin, qmax, kid + tid * (BN + 1));
+      cls = composed ? classify_tile_composed(m, b, qlo, bidx * BN, BM, BN, uniform, q0, qid, qturn, qdoc)
+                     : classify_tile(m, b, qlo, bidx * BN, BM, BN, qid, qmin, qmax, kid + tid * (BN + 1));
       t.tile_class[rowoff + bidx] = cls;
     }
     const uint64_t fm = __ballot(cls == BMATTN_TILE_FULL);

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define BMATTN_ABI_VERSION 1
+#define BMATTN_ABI_VERSION 2
 
 /* ---- status codes ----------------------------------------------------- */
 typedef enum {
@@ -69,15 +69,38 @@ typedef enum {
  *   STRIP_THINKING  j <= p(i) and not (role_k[j] == think_role and
  *                                       turn_k[j] < turn_q[i])
  *                                                           [XORL "Mask specifications"]
+ *   COMPOSED        the AND of the terms set in desc->terms:
+ *     BMATTN_TERM_CAUSAL          j <= p(i)
+ *     BMATTN_TERM_DOCUMENT        doc_k[j] == doc_q[i] and doc_k[j] >= 0
+ *                                 (a negative document id marks padding)
+ *     BMATTN_TERM_SHARED_PREFIX   seg_k[j] == 0 or seg_k[j] == seg_q[i]
+ *     BMATTN_TERM_STRIP_THINKING  not (role_k[j] == think_role and
+ *                                      turn_k[j] < turn_q[i])
+ *                                 [XORL "Proposed work" 3: composable causal,
+ *                                  document, shared-prefix and strip-thinking
+ *                                  pieces; "Current state in this tree":
+ *                                  causal + document + padding in one mask]
+ *   (CAUSAL is COMPOSED with {CAUSAL}, SHARED_PREFIX with {CAUSAL,
+ *   SHARED_PREFIX}, STRIP_THINKING with {CAUSAL, STRIP_THINKING}.)
  * Packed documents are sequences of cu_seqlens with the CAUSAL kind: every
- * document gets its own causal square and nothing off it.
+ * document gets its own causal square and nothing off it; the DOCUMENT term
+ * expresses the same inside one sequence.
  */
 typedef enum {
   BMATTN_MASK_FULL = 0,
   BMATTN_MASK_CAUSAL = 1,
   BMATTN_MASK_SHARED_PREFIX = 2,
-  BMATTN_MASK_STRIP_THINKING = 3
+  BMATTN_MASK_STRIP_THINKING = 3,
+  BMATTN_MASK_COMPOSED = 4
 } bmattn_mask_kind;
+
+/* Terms of a COMPOSED mask (bit set in bmattn_mask_desc.terms). */
+enum {
+  BMATTN_TERM_CAUSAL = 1,
+  BMATTN_TERM_DOCUMENT = 2,
+  BMATTN_TERM_SHARED_PREFIX = 4,
+  BMATTN_TERM_STRIP_THINKING = 8
+};
 
 typedef enum { BMATTN_F32 = 0, BMATTN_BF16 = 1 } bmattn_dtype;
 
@@ -94,7 +117,8 @@ enum { BMATTN_TILE_EMPTY = 0, BMATTN_TILE_PARTIAL = 1, BMATTN_TILE_FULL = 2 };
  * Id arrays are indexed by packed query row (…_q) or packed key row (…_k);
  * for self-attention pass the same array for both sides.  Only the ids the
  * kind reads must be non-NULL (SHARED_PREFIX: seg_q, seg_k; STRIP_THINKING:
- * role_k, turn_q, turn_k).
+ * role_k, turn_q, turn_k; COMPOSED: those of its terms, DOCUMENT: doc_q,
+ * doc_k).
  */
 typedef struct {
   int32_t kind;           /* bmattn_mask_kind                                  */
@@ -104,7 +128,7 @@ typedef struct {
   int64_t total_q;        /* cu_seqlens_q[n_seqs]: rows of Q, O, ids_q         */
   int64_t total_k;        /* cu_seqlens_k[n_seqs]: rows of K, V, ids_k         */
   int32_t think_role;     /* role value of think tokens (STRIP_THINKING)       */
-  int32_t reserved0;
+  int32_t terms;          /* COMPOSED: OR of BMATTN_TERM_* (non-zero); else 0  */
   const int32_t* cu_seqlens_q; /* [n_seqs + 1], non-decreasing, starts at 0   */
   const int32_t* cu_seqlens_k; /* [n_seqs + 1], non-decreasing, starts at 0   */
   const int32_t* seg_q;   /* [total_q] segment id of each query (0 = prefix)   */
@@ -112,6 +136,8 @@ typedef struct {
   const int32_t* role_k;  /* [total_k] role of each key                        */
   const int32_t* turn_q;  /* [total_q] turn of each query                      */
   const int32_t* turn_k;  /* [total_k] turn of each key                        */
+  const int32_t* doc_q;   /* [total_q] document of each query (< 0: padding)   */
+  const int32_t* doc_k;   /* [total_k] document of each key (< 0: padding)     */
 } bmattn_mask_desc;
 
 /* ---- block mask ------------------------------------------------------------

@@ -29,7 +29,8 @@ def desc_for(layout, device=DEV) -> bm.MaskDesc:
                               seg_k=layout.seg_k, role_q=layout.role_q, role_k=layout.role_k,
                               turn_q=layout.turn_q, turn_k=layout.turn_k,
                               think_role=layout.think_role, loss_role=layout.loss_role,
-                              history_role=layout.history_role)
+                              history_role=layout.history_role, doc_q=layout.doc_q,
+                              doc_k=layout.doc_k, terms=layout.terms)
 
 
 def oracle_tiles(layout, BM, BN):

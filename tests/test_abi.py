@@ -32,16 +32,16 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     L = bm.lib()
-    assert L.bmattn_abi_version() == 1
+    assert L.bmattn_abi_version() == 2
     assert L.bmattn_status_string(0) == b"ok"
     assert L.bmattn_status_string(2) == b"unsupported configuration"
     assert L.bmattn_status_string(99) == b"unknown status"
 
 
-def _desc(kind=bm.MASK_CAUSAL, n=2, mq=100, mk=100, tq=150, tk=150, ids=True):
-    d = bm.MaskDescC(kind, n, mq, mk, tq, tk, 1, 0, FAKE, FAKE,
-                     FAKE if ids else None, FAKE if ids else None, FAKE if ids else None,
-                     FAKE if ids else None, FAKE if ids else None)
+def _desc(kind=bm.MASK_CAUSAL, n=2, mq=100, mk=100, tq=150, tk=150, ids=True, terms=0, docs=True):
+    i = FAKE if ids else None
+    dd = FAKE if docs else None
+    d = bm.MaskDescC(kind, n, mq, mk, tq, tk, 1, terms, FAKE, FAKE, i, i, i, i, i, dd, dd)
     return d
 
 
@@ -179,6 +179,25 @@ def test_gather_and_debug_and_validate_rejections():
     assert L.bmattn_validate(ctypes.byref(d), FAKE, 0, 16, 10, FAKE, None) == 1
 
 
+@pytest.mark.parametrize("terms,docs,ids,ok", [
+    (1, True, True, True), (15, True, True, True), (2, True, False, True),
+    (0, True, True, False),    # COMPOSED needs at least one term
+    (16, True, True, False),   # unknown term bit
+    (-1, True, True, False),
+    (2, False, True, False),   # DOCUMENT without doc arrays
+    (4, True, False, False),   # SHARED_PREFIX without segments
+    (8, True, False, False),   # STRIP_THINKING without roles / turns
+])
+def test_composed_description_validation(terms, docs, ids, ok):
+    rc, *_ = _call_shape(_desc(kind=bm.MASK_COMPOSED, terms=terms, docs=docs, ids=ids), 128, 64)
+    assert (rc == 0) == ok, bm.lib().bmattn_last_error()
+
+
+def test_terms_rejected_on_plain_kinds():
+    rc, *_ = _call_shape(_desc(kind=bm.MASK_CAUSAL, terms=1), 128, 64)
+    assert rc == 1 and b"terms must be 0" in bm.lib().bmattn_last_error()
+
+
 def test_duplicated_answer_ids_rejected_before_launch():
     L = bm.lib()
     f = ctypes.c_void_p(FAKE)
@@ -214,7 +233,8 @@ def test_struct_layouts_match_the_header(tmp_path):
     if cc is None:
         pytest.skip("no host C compiler")
     checks = {
-        "bmattn_mask_desc": (bm.MaskDescC, ["kind", "think_role", "cu_seqlens_q", "turn_k"]),
+        "bmattn_mask_desc": (bm.MaskDescC, ["kind", "think_role", "terms", "cu_seqlens_q", "turn_k",
+                                            "doc_q", "doc_k"]),
         "bmattn_block_mask": (bm.BlockMaskC, ["block_m", "tile_class", "row_order"]),
         "bmattn_block_mask_cols": (bm.BlockMaskColsC, ["block_m", "full_cnt", "col_order"]),
         "bmattn_fwd_args": (bm.FwdArgsC, ["q", "lse", "block_table", "scale", "workspace_bytes"]),

@@ -20,6 +20,7 @@ def _count(lay):
     synth.strip_thinking(n_turns=3, user=2, think=5, answer=3, H=1, D=8),
     synth.strip_thinking_duplicated(n_turns=3, user=2, think=5, answer=3, H=1, D=8),
     synth.strip_thinking_duplicated(n_turns=4, user=1, think=0, answer=2, H=1, D=8),
+    synth.shared_prefix_groups(n_groups=3, prefix=5, n_suffix=2, suffix=4, pad=3, H=1, D=8),
     synth.paged_decode(seed=1, n_seqs=5, lo=3, hi=50, H=1, D=8),
     synth.Layout("x", "causal", "f32", 1, 8, [3, 5, 1], [7, 5, 2]),
 ])
@@ -39,4 +40,9 @@ def test_closed_forms_named_workloads():
 
 def test_closed_form_duplicated_answers_full_size():
     lay = synth.config("strip_thinking_duplicated")
+    assert bench.visible_pairs(lay) == _count(lay)
+
+
+def test_closed_form_shared_prefix_groups_full_size():
+    lay = synth.config("shared_prefix_groups")
     assert bench.visible_pairs(lay) == _count(lay)

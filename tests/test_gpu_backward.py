@@ -131,7 +131,7 @@ def test_backward_packed_documents_full_size():
                 "packed_documents heads 0,7,15")
 
 
-@pytest.mark.parametrize("name", ["shared_prefix", "strip_thinking"])
+@pytest.mark.parametrize("name", ["shared_prefix", "strip_thinking", "shared_prefix_groups"])
 def test_backward_single_sequence_workloads_one_head(name):
     lay = synth.config(name)
     say(f"backward {name} full size")

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 SHAPES = [(1, 1), (2, 3), (4, 4), (13, 8), (16, 64), (64, 16), (128, 64), (1, 64), (37, 29),
           (128, 128), (256, 64)]
 KIND_SEED = {"full": 1, "causal": 2, "shared_prefix": 3, "strip_thinking": 4,
-             "strip_thinking_duplicated": 5}
+             "strip_thinking_duplicated": 5, "composed": 6}
 
 
 @pytest.mark.parametrize("decode_q", [None, 1, 3])
@@ -43,7 +43,8 @@ def test_tiles_empty_and_tiny_sequences():
 
 
 @pytest.mark.parametrize("name", ["causal_f32", "packed_documents", "shared_prefix",
-                                  "strip_thinking", "strip_thinking_duplicated"])
+                                  "strip_thinking", "strip_thinking_duplicated",
+                                  "shared_prefix_groups"])
 def test_tiles_bit_exact_named_workloads(name):
     lay = synth.config(name)
     desc = _hip.desc_for(lay)
@@ -199,3 +200,39 @@ def test_duplicated_answer_ids_in_place():
     bm.relabel(d1)
     torch.cuda.synchronize()
     assert torch.equal(d1.role_k, before[0]) and torch.equal(d1.turn_q, before[1])
+
+
+@pytest.mark.parametrize("terms", [("causal",), ("document",), ("causal", "document"),
+                                   ("causal", "shared_prefix"), ("causal", "strip_thinking"),
+                                   ("document", "shared_prefix", "strip_thinking"),
+                                   ("causal", "document", "shared_prefix", "strip_thinking")])
+def test_composed_every_term_set(terms):
+    # Each term set on random layouts (with padding and several documents).
+    rng = np.random.default_rng(sum(bm.TERM_CODES[t] for t in terms) * 31 + len(terms))
+    for trial in range(2):
+        lay = synth.random_layout(rng, "composed", n_seqs=3, max_len=200)
+        lay.terms = terms
+        desc = _hip.desc_for(lay)
+        for BM, BN in ((128, 64), (64, 128), (16, 16), (1, 64)):
+            say(f"composed terms={terms} trial={trial} lens={lay.seqlens_k} {BM}x{BN}")
+            t = _hip.check_tiles(lay, desc, BM, BN)
+            _hip.check_dense(lay, desc, t)
+
+
+def test_composed_single_terms_match_plain_kinds_bit_exact():
+    # {causal, shared_prefix} over the same ids builds the same block mask as
+    # the SHARED_PREFIX kind; likewise strip-thinking and causal.
+    rng = np.random.default_rng(77)
+    for kind, terms in (("causal", ("causal",)), ("shared_prefix", ("causal", "shared_prefix")),
+                        ("strip_thinking", ("causal", "strip_thinking"))):
+        lay = synth.random_layout(rng, kind, n_seqs=3, max_len=400)
+        plain = _hip.desc_for(lay)
+        comp = bm.MaskDesc.create("composed", lay.cu_q, lay.cu_k, lay.max_q, lay.max_k, device=DEV,
+                                  seg_q=lay.seg_q, seg_k=lay.seg_k, role_k=lay.role_k,
+                                  turn_q=lay.turn_q, turn_k=lay.turn_k, terms=terms)
+        say(f"composed {terms} vs plain {kind}")
+        a = bm.build_block_mask(plain, 128, 64)
+        b = bm.build_block_mask(comp, 128, 64)
+        torch.cuda.synchronize()
+        for f in ("tile_class", "full_cnt", "part_cnt", "full_idx", "part_idx", "row_order"):
+            assert torch.equal(getattr(a, f), getattr(b, f)), (kind, f)
