@@ -123,15 +123,29 @@ __device__ uint8_t classify_tile(const MaskDev& m, const SeqBounds& b, int qlo, 
   return any_hid ? BMATTN_TILE_PARTIAL : BMATTN_TILE_FULL;
 }
 
-// COMPOSED masks: q ids of the tile's rows in qs / qt / qd (segment, turn,
-// document); `uniform` when every row of the tile that lies in the
-// sequence carries the ids q0.  Then a key is visible to all of them or to
-// none apart from the causal term, and the tiles that the causal term does
-// not cut follow from "every key" / "any key"; other tiles enumerate their
-// pairs until they see a visible and a hidden one.
-__device__ uint8_t classify_tile_composed(const MaskDev& m, const SeqBounds& b, int qlo, int klo,
-                                          int BM, int BN, bool uniform, QIds q0,
-                                          const int32_t* qs, const int32_t* qt, const int32_t* qd) {
+// COMPOSED masks.  The queries of a row tile fall into a few groups of
+// equal ids (segment, turn, document); the kernel lists them (up to
+// kMaxGroups, with the largest row of each) before classifying.  With the
+// causal term, pair (i, j) is visible iff j <= i + off and the key's ids
+// pass the group's id terms, so a tile is
+//   EMPTY  iff for every key j and group g: the ids fail, or j > hi_g + off;
+//   FULL   iff it lies inside the sequence, the causal term cuts none of its
+//          pairs (klo + BN - 1 <= qlo + off) and every key passes every group;
+// exactly the classes of the element predicate.  The staging pass stores,
+// per key, the bit mask of the groups whose ids it passes (one byte), so a
+// tile costs one byte per key.  Rows with more groups enumerate their pairs
+// (key ids from LDS: four arrays of kw words, segment, role, turn, document).
+constexpr int kMaxGroups = 8;
+
+struct RowGroups {
+  int n;                        // number of groups, -1 when over kMaxGroups
+  QIds ids[kMaxGroups];
+  int hi[kMaxGroups];           // largest row (inside the sequence) of each group
+};
+
+__device__ uint8_t classify_tile_groups(const MaskDev& m, const SeqBounds& b, int qlo, int klo,
+                                        int BM, int BN, int n, const int* hi,
+                                        const uint8_t* okb, int k0) {
   if (qlo >= b.lq || klo >= b.lk) return BMATTN_TILE_EMPTY;
   const int qhi = min(qlo + BM, b.lq);
   const int khi = min(klo + BN, b.lk);
@@ -140,24 +154,41 @@ __device__ uint8_t classify_tile_composed(const MaskDev& m, const SeqBounds& b, 
   const int64_t off = (int64_t)b.lk - b.lq;
   if (causal && (int64_t)klo > (int64_t)(qhi - 1) + off) return BMATTN_TILE_EMPTY;
   const bool causal_full = !causal || ((int64_t)klo + BN - 1 <= (int64_t)qlo + off);
-  if (uniform && causal_full) {
-    bool all = true, any = false;
-    for (int j = klo; j < khi; ++j) {
-      const KIds k = load_kids(m, b, j);
-      const bool ok = composed_ids_ok(m.terms, m.think_role, q0, k.a, k.b, k.c, k.d);
-      all &= ok;
-      any |= ok;
+  const uint32_t every = (1u << n) - 1u;
+  bool all = inside && causal_full, any = false;
+  for (int j = klo; j < khi; ++j) {
+    const uint32_t ok = okb[j - k0];
+    uint32_t reach = every;  // groups with a row that the causal term lets see key j
+    if (causal) {
+      reach = 0;
+      for (int g = 0; g < n; ++g) reach |= (uint32_t)((int64_t)j <= (int64_t)hi[g] + off) << g;
     }
-    if (!any) return BMATTN_TILE_EMPTY;
-    return (all && inside) ? BMATTN_TILE_FULL : BMATTN_TILE_PARTIAL;
+    all &= ok == every;
+    any |= (ok & reach) != 0;
+    if (any && !all) return BMATTN_TILE_PARTIAL;
   }
+  if (!any) return BMATTN_TILE_EMPTY;
+  return all ? BMATTN_TILE_FULL : BMATTN_TILE_PARTIAL;
+}
+
+__device__ uint8_t classify_tile_enum(const MaskDev& m, const SeqBounds& b, int qlo, int klo,
+                                      int BM, int BN, const int32_t* qs, const int32_t* qt,
+                                      const int32_t* qd, const int32_t* kid, int kw, int k0) {
+  if (qlo >= b.lq || klo >= b.lk) return BMATTN_TILE_EMPTY;
+  const int qhi = min(qlo + BM, b.lq);
+  const int khi = min(klo + BN, b.lk);
+  const bool inside = (qlo + BM <= b.lq) && (klo + BN <= b.lk);
+  const bool causal = (m.terms & BMATTN_TERM_CAUSAL) != 0;
+  const int64_t off = (int64_t)b.lk - b.lq;
+  if (causal && (int64_t)klo > (int64_t)(qhi - 1) + off) return BMATTN_TILE_EMPTY;
   bool any_vis = false, any_hid = !inside;
   for (int j = klo; j < khi; ++j) {
-    const KIds k = load_kids(m, b, j);
+    const int u = j - k0;
+    const int32_t a0 = kid[u], a1 = kid[kw + u], a2 = kid[2 * kw + u], a3 = kid[3 * kw + u];
     for (int i = qlo; i < qhi; ++i) {
       const QIds q{qs[i - qlo], qt[i - qlo], qd[i - qlo]};
       const bool v = (!causal || (int64_t)j <= off + i) &&
-                     composed_ids_ok(m.terms, m.think_role, q, k.a, k.b, k.c, k.d);
+                     composed_ids_ok(m.terms, m.think_role, q, a0, a1, a2, a3);
       any_vis |= v;
       any_hid |= !v;
       if (any_vis && any_hid) return BMATTN_TILE_PARTIAL;
@@ -172,6 +203,7 @@ __device__ uint8_t classify_tile_composed(const MaskDev& m, const SeqBounds& b, 
 // Staged key ids per chunk: tiles of BN keys, each run padded to BN + 1
 // words so that lanes scanning different tiles hit different LDS banks.
 constexpr int kKidKeys = 16384;
+constexpr int kStageBatch = 8;
 
 __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev t) {
   __shared__ int32_t qid[kMaxBlock];
@@ -187,8 +219,7 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev 
   const int qlo = a * BM;
 
   const bool composed = m.kind == BMATTN_MASK_COMPOSED;
-  const QIds q0 = load_qids(m, b, qlo);
-  int same = 1;
+  __shared__ RowGroups rg;
   // Row ids (segment for shared-prefix, turn for strip-thinking) and range.
   int32_t lmin = INT32_MAX, lmax = INT32_MIN;
   for (int i = tid; i < BM; i += kThreads) {
@@ -198,7 +229,6 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev 
     if (composed) {
       qturn[i] = x.turn;
       qdoc[i] = x.doc;
-      if (qlo + i < b.lq) same &= (x.seg == q0.seg) & (x.turn == q0.turn) & (x.doc == q0.doc);
     }
     if (qlo + i < b.lq) {
       lmin = min(lmin, v);
@@ -220,30 +250,128 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev 
     qmax = max(qmax, red[1][w]);
   }
 
-  // COMPOSED: do all the row's queries carry the ids of its first one?
-  const bool uniform = __syncthreads_and(same) != 0;
+  // COMPOSED: the groups of equal query ids.  Row i's leader is the first
+  // row with its ids; leaders, in row order, number the groups (more than
+  // kMaxGroups: none, enumerate), and each group's largest row is an LDS
+  // maximum over its rows.
+  if (composed) {
+    __shared__ int32_t lead[kMaxBlock];
+    __shared__ int32_t nlead;
+    const int nrows = max(0, min(BM, b.lq - qlo));
+    if (tid == 0) nlead = 0;
+    for (int i = tid; i < nrows; i += kThreads) {
+      int r = 0;
+      while (!(qid[r] == qid[i] && qturn[r] == qturn[i] && qdoc[r] == qdoc[i])) ++r;
+      lead[i] = r;
+    }
+    __syncthreads();
+    // leaders in row order: chunked ballots over the rows
+    for (int i0 = 0; i0 < nrows; i0 += kThreads) {
+      const int i = i0 + tid;
+      const bool isl = i < nrows && lead[i] == i;
+      const uint64_t bm = __ballot(isl);
+      const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      if (lane == 0) wave_tot[0][wave] = __popcll(bm);
+      __syncthreads();
+      int base = nlead;
+      for (int w = 0; w < wave; ++w) base += wave_tot[0][w];
+      if (isl) {
+        const int g = base + __popcll(bm & lt);
+        lead[i] = -1 - g;  // a leader holds its group number, encoded below 0
+        if (g < kMaxGroups) {
+          rg.ids[g] = QIds{qid[i], qturn[i], qdoc[i]};
+          rg.hi[g] = qlo + i;  // rows of the sequence, as the tile bounds
+        }
+      }
+      __syncthreads();
+      if (tid == 0) for (int w = 0; w < kThreads / 64; ++w) nlead += wave_tot[0][w];
+      __syncthreads();
+    }
+    for (int i = tid; i < nrows; i += kThreads) {
+      const int l = lead[i];
+      const int g = l < 0 ? -1 - l : -1 - lead[l];
+      if (g < kMaxGroups) atomicMax(&rg.hi[g], qlo + i);
+    }
+    if (tid == 0) rg.n = nlead <= kMaxGroups ? nlead : -1;
+    __syncthreads();
+  }
 
   const int64_t rowoff = (int64_t)row * t.n_kt;
   int full_base = 0, part_base = 0;
   // Chunks of tpc kv tiles, one per thread; for the id-based kinds the ids of
   // the chunk's keys are first staged in LDS with coalesced loads.
   const bool ids = m.kind == BMATTN_MASK_SHARED_PREFIX || m.kind == BMATTN_MASK_STRIP_THINKING;
-  const int tpc = std::max(1, std::min(kThreads, kKidKeys / BN));
+  // COMPOSED stages one group byte per key (kKidKeys * 4 keys per chunk) or,
+  // for rows with too many groups, four arrays of kw keys.
+  const int kw = kKidKeys / 4;
+  const bool groups = composed && rg.n >= 0;
+  const int ckeys = !composed ? kKidKeys : (groups ? 4 * kKidKeys : kw);
+  const int tpc = std::max(1, std::min(kThreads, ckeys / BN));
+  uint8_t* okb = reinterpret_cast<uint8_t*>(kid);
+  const int ng = composed ? rg.n : 0;
+  // With the causal term no key past the row's last query position is
+  // visible: those tiles classify as EMPTY without reading ids, so their
+  // ids are not staged.
+  int64_t kvis = b.lk;
+  if ((m.terms & BMATTN_TERM_CAUSAL) && qlo < b.lq)
+    kvis = std::min<int64_t>(b.lk, (int64_t)std::min(qlo + BM, b.lq) + ((int64_t)b.lk - b.lq));
   for (int c0 = 0; c0 < t.n_kt; c0 += tpc) {
     const int bidx = c0 + tid;
     const int kid0 = c0 * BN;
+    // Staging loops take kStageBatch keys per thread per pass, all loads of
+    // a pass issued before their first use.
     if (ids) {
-      const int kend = (int)std::min<int64_t>((int64_t)(c0 + tpc) * BN, b.lk);
-      for (int j = kid0 + tid; j < kend; j += kThreads) {
+      const int kend = (int)std::max<int64_t>(0, std::min<int64_t>((int64_t)(c0 + tpc) * BN, kvis));
+      for (int j0 = kid0 + tid; j0 < kend; j0 += kStageBatch * kThreads) {
+        int32_t v[kStageBatch];
+#pragma unroll
+        for (int e = 0; e < kStageBatch; ++e) {
+          const int j = j0 + e * kThreads;
+          v[e] = j < kend ? staged_kid(m, b, j) : 0;
+        }
+#pragma unroll
+        for (int e = 0; e < kStageBatch; ++e) {
+          const int u = j0 + e * kThreads - kid0;
+          if (j0 + e * kThreads < kend) kid[u + u / BN] = v[e];
+        }
+      }
+      __syncthreads();
+    }
+    if (composed) {
+      const int kend = (int)std::max<int64_t>(0, std::min<int64_t>((int64_t)(c0 + tpc) * BN, kvis));
+      for (int j0 = kid0 + tid; j0 < kend; j0 += kStageBatch * kThreads) {
+       KIds kb[kStageBatch];
+#pragma unroll
+       for (int e = 0; e < kStageBatch; ++e) {
+         const int j = j0 + e * kThreads;
+         kb[e] = j < kend ? load_kids(m, b, j) : KIds{0, 0, 0, 0};
+       }
+#pragma unroll
+       for (int e = 0; e < kStageBatch; ++e) {
+        const int j = j0 + e * kThreads;
+        if (j >= kend) continue;
+        const KIds k = kb[e];
         const int u = j - kid0;
-        kid[u + u / BN] = staged_kid(m, b, j);
+        if (groups) {
+          uint32_t ok = 0;
+          for (int g = 0; g < ng; ++g)
+            ok |= (uint32_t)composed_ids_ok(m.terms, m.think_role, rg.ids[g], k.a, k.b, k.c, k.d) << g;
+          okb[u] = (uint8_t)ok;
+        } else {
+          kid[u] = k.a;
+          kid[kw + u] = k.b;
+          kid[2 * kw + u] = k.c;
+          kid[3 * kw + u] = k.d;
+        }
+       }
       }
       __syncthreads();
     }
     uint8_t cls = BMATTN_TILE_EMPTY;
     if (tid < tpc && bidx < t.n_kt) {
-      cls = composed ? classify_tile_composed(m, b, qlo, bidx * BN, BM, BN, uniform, q0, qid, qturn, qdoc)
-                     : classify_tile(m, b, qlo, bidx * BN, BM, BN, qid, qmin, qmax, kid + tid * (BN + 1));
+      cls = groups     ? classify_tile_groups(m, b, qlo, bidx * BN, BM, BN, ng, rg.hi, okb, kid0)
+            : composed ? classify_tile_enum(m, b, qlo, bidx * BN, BM, BN, qid, qturn, qdoc, kid, kw, kid0)
+                       : classify_tile(m, b, qlo, bidx * BN, BM, BN, qid, qmin, qmax, kid + tid * (BN + 1));
       t.tile_class[rowoff + bidx] = cls;
     }
     const uint64_t fm = __ballot(cls == BMATTN_TILE_FULL);
