@@ -1,4 +1,4 @@
-"""Block-sparse masked attention forward for AMD MI355X (gfx950).
+"""Block-sparse masked attention (forward and backward) for AMD MI355X (gfx950).
 
 The computation lives in the HIP library ``lib/libbmattn.so`` (C ABI in
 include/bmattn.h); ``bmattn`` is its ctypes binding.  Build it with
@@ -21,4 +21,10 @@ from .bmattn import (  # noqa: F401
     forward_workspace_size,
     paged_gather,
     validate,
+    transpose_block_mask,
+    build_backward_cols,
+    backward,
+    backward_workspace_size,
+    duplicated_answer_ids,
+    relabel,
 )

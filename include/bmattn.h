@@ -1,5 +1,6 @@
 /*
- * bmattn -- block-sparse masked attention forward for AMD MI355X (gfx950).
+ * bmattn -- block-sparse masked attention (forward and backward) for AMD MI355X
+ * (gfx950).
  *
  * C ABI.  Plain pointers and sizes only.  Every buffer is owned by the
  * caller; device buffers are plain HIP device allocations.  Every call is
