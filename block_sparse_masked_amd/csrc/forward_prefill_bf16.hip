@@ -32,7 +32,9 @@
 //  * the next tile's copies are issued one per 16-d step of the current
 //    tile's S product, between its MFMA pairs, and waited for only at the
 //    end of the iteration: one barrier per tile.  The list entry two tiles
-//    ahead is loaded early and read after that barrier;
+//    ahead is loaded early and read after that barrier, and so are the
+//    first four K fragments of the next tile, so that their LDS latency
+//    runs beside the P V MFMAs still in flight;
 //  * exponentials are base 2 with log2(e) folded into the softmax scale, and
 //    the reference max moves only when it would grow by more than 8.
 #include <hip/hip_runtime.h>
@@ -259,23 +261,39 @@ struct TileCopies {
   uint32_t klds, vlds;  // LDS byte addresses of the wave's first K / V slot
 };
 // S^T = K Q^T for the tile's two 32-key blocks, K fragments read a few
-// steps ahead.  With COPIES, the wave's copies of the next (whole) tile are
+// steps ahead (the first steps' fragments come in `kp`, read by the caller).  With COPIES, the wave's copies of the next (whole) tile are
 // issued one per 16-d step, after that step's two MFMAs: a copy that has to
 // wait for the memory pipeline then waits beside running matrix work.
+// The K fragments of a tile's first (up to four) 16-d steps, both 32-key
+// blocks.
+template <int D>
+struct KPre {
+  static constexpr int N = (D / 16) < 4 ? (D / 16) : 4;
+  bf16x8 k0[N], k1[N];
+};
+template <int D>
+__device__ __forceinline__ void k_prefetch(const char* Ks, const Addr<D>& ad, KPre<D>& kp) {
+#pragma unroll
+  for (int ks = 0; ks < KPre<D>::N; ++ks) {
+    kp.k0[ks] = *reinterpret_cast<const bf16x8*>(Ks + ad.k[ks]);
+    kp.k1[ks] = *reinterpret_cast<const bf16x8*>(Ks + ad.k[ks] + 32 * Lay<D>::kRowB);
+  }
+}
 template <int D, bool COPIES>
 __device__ __forceinline__ void s_product(const char* Ks, const bf16x8 (&q)[D / 16], const Addr<D>& ad,
-                                          f32x16& s0, f32x16& s1, const TileCopies<D>& tc) {
+                                          f32x16& s0, f32x16& s1, const TileCopies<D>& tc,
+                                          const KPre<D>& kp) {
   using L = Lay<D>;
   constexpr int N = D / 16;
-  constexpr int kAhead = N < 4 ? N : 4;
+  constexpr int kAhead = KPre<D>::N;
   static_assert(2 * L::kCopies == N, "one copy per 16-d step");
   bf16x8 k0[N], k1[N];
   s0 = f32x16{};
   s1 = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < kAhead; ++ks) {
-    k0[ks] = *reinterpret_cast<const bf16x8*>(Ks + ad.k[ks]);
-    k1[ks] = *reinterpret_cast<const bf16x8*>(Ks + ad.k[ks] + 32 * L::kRowB);
+    k0[ks] = kp.k0[ks];
+    k1[ks] = kp.k1[ks];
   }
 #pragma unroll
   for (int ks = 0; ks < N; ++ks) {
@@ -474,7 +492,8 @@ __device__ __forceinline__ void kv_step(const char* cur, char* nxt, bool has_nex
                                         const FwdDev& p, const SeqBounds& sb,
                                         int s, int h, int gw, int lane, const bf16x8 (&q)[D / 16],
                                         const Addr<D>& ad, const Copy<D, PAGED, COMP>& cp,
-                                        RowState<D>& st, int qi, QIds qids, int g) {
+                                        RowState<D>& st, int qi, QIds qids, int g,
+                                        const KPre<D>& kp) {
   using L = Lay<D>;
   const bool whole = has_next && cp.whole(sb, ktn);
   if (has_next && !whole) cp.tile(p, sb, s, h, ktn, MASKED || mnext, gw, lane, nxt);
@@ -493,8 +512,8 @@ __device__ __forceinline__ void kv_step(const char* cur, char* nxt, bool has_nex
   tc.klds = lds_addr(nxt + gw * L::kCopies * 1024);
   tc.vlds = lds_addr(nxt + L::kV + gw * L::kCopies * 1024);
   f32x16 s0, s1;
-  if (whole) s_product<D, true>(cur, q, ad, s0, s1, tc);
-  else s_product<D, false>(cur, q, ad, s0, s1, tc);
+  if (whole) s_product<D, true>(cur, q, ad, s0, s1, tc, kp);
+  else s_product<D, false>(cur, q, ad, s0, s1, tc, kp);
   bf16x8 pf[4];
   softmax_update<D, MASKED, COMP>(s0, s1, pf, st, cur, p, sb, kt, qi, qids, g);
   pv_product<D>(cur, pf, st, ad);
@@ -589,6 +608,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(FwdDev p) {
     if (ntiles > 1) kt_nxt = *entry_ptr(1);
   }
   end_of_tile();
+  // The first K fragments of the next tile are read right after each
+  // barrier, ahead of the previous tile's remaining P V MFMAs.
+  KPre<D> kp;
+  k_prefetch<D>(smem, ad, kp);
 
   // Iteration t handles list entry t: FULL tiles first (no mask code), then
   // the PARTIAL ones.  One barrier per tile.
@@ -599,8 +622,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(FwdDev p) {
     int kt_ahead;
     kv_step<D, PAGED, false, COMP>(smem + (t & 1) * L::kStage, smem + ((t + 1) & 1) * L::kStage, has_next,
                              mnext, kt_nxt, kt_cur, entry_ptr(t + 2), kt_ahead, p, sb, s, h, wave,
-                             lane, q, ad, cp, st, qi, qids, g);
+                             lane, q, ad, cp, st, qi, qids, g, kp);
     end_of_tile();
+    k_prefetch<D>(smem + ((t + 1) & 1) * L::kStage, ad, kp);
     kt_cur = kt_nxt;
     kt_nxt = uniform_after_wait(kt_ahead);
   }
@@ -608,8 +632,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(FwdDev p) {
     int kt_ahead;
     kv_step<D, PAGED, true, COMP>(smem + (t & 1) * L::kStage, smem + ((t + 1) & 1) * L::kStage,
                             t + 1 < ntiles, true, kt_nxt, kt_cur, entry_ptr(t + 2), kt_ahead, p, sb,
-                            s, h, wave, lane, q, ad, cp, st, qi, qids, g);
+                            s, h, wave, lane, q, ad, cp, st, qi, qids, g, kp);
     end_of_tile();
+    k_prefetch<D>(smem + ((t + 1) & 1) * L::kStage, ad, kp);
     kt_cur = kt_nxt;
     kt_nxt = uniform_after_wait(kt_ahead);
   }
