@@ -171,6 +171,29 @@ __device__ uint8_t classify_tile_groups(const MaskDev& m, const SeqBounds& b, in
   return all ? BMATTN_TILE_FULL : BMATTN_TILE_PARTIAL;
 }
 
+// A COMPOSED tile from the AND / OR of its keys' group bytes, when every
+// group's causal reach covers the whole tile and all its keys were staged
+// (then a key's reachable groups are all groups); otherwise key by key.
+__device__ uint8_t classify_tile_summary(const MaskDev& m, const SeqBounds& b, int qlo, int klo,
+                                         int BM, int BN, int n, int hmin, uint32_t tand,
+                                         uint32_t tor, int tcnt, const int* hi, const uint8_t* okb,
+                                         int k0) {
+  if (qlo >= b.lq || klo >= b.lk) return BMATTN_TILE_EMPTY;
+  const int qhi = min(qlo + BM, b.lq);
+  const int khi = min(klo + BN, b.lk);
+  const bool causal = (m.terms & BMATTN_TERM_CAUSAL) != 0;
+  const int64_t off = (int64_t)b.lk - b.lq;
+  if (causal && (int64_t)klo > (int64_t)(qhi - 1) + off) return BMATTN_TILE_EMPTY;
+  if ((!causal || (int64_t)hmin + off >= (int64_t)khi - 1) && tcnt == khi - klo) {
+    const bool inside = (qlo + BM <= b.lq) && (klo + BN <= b.lk);
+    const bool causal_full = !causal || ((int64_t)klo + BN - 1 <= (int64_t)qlo + off);
+    const uint32_t every = (1u << n) - 1u;
+    if ((tor & every) == 0) return BMATTN_TILE_EMPTY;
+    return (inside && causal_full && (tand & every) == every) ? BMATTN_TILE_FULL : BMATTN_TILE_PARTIAL;
+  }
+  return classify_tile_groups(m, b, qlo, klo, BM, BN, n, hi, okb, k0);
+}
+
 __device__ uint8_t classify_tile_enum(const MaskDev& m, const SeqBounds& b, int qlo, int klo,
                                       int BM, int BN, const int32_t* qs, const int32_t* qt,
                                       const int32_t* qd, const int32_t* kid, int kw, int k0) {
@@ -309,6 +332,14 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev 
   const int tpc = std::max(1, std::min(kThreads, ckeys / BN));
   uint8_t* okb = reinterpret_cast<uint8_t*>(kid);
   const int ng = composed ? rg.n : 0;
+  // COMPOSED groups: per tile of the chunk, the AND and OR of its keys'
+  // group bytes and the number of keys staged; the smallest group end row.
+  __shared__ uint8_t tand[kThreads], tor[kThreads];
+  __shared__ int16_t tcnt[kThreads];
+  // (only for 64-key tiles: one wave's lanes then cover one tile)
+  const bool summ = groups && BN == 64;
+  int hmin = INT32_MAX;
+  for (int gi = 0; gi < ng; ++gi) hmin = min(hmin, rg.hi[gi]);
   // With the causal term no key past the row's last query position is
   // visible: those tiles classify as EMPTY without reading ids, so their
   // ids are not staged.
@@ -339,6 +370,8 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev 
     }
     if (composed) {
       const int kend = (int)std::max<int64_t>(0, std::min<int64_t>((int64_t)(c0 + tpc) * BN, kvis));
+      if (summ && tid < tpc) tcnt[tid] = 0;
+      if (summ) __syncthreads();
       for (int j0 = kid0 + tid; j0 < kend; j0 += kStageBatch * kThreads) {
        KIds kb[kStageBatch];
 #pragma unroll
@@ -364,12 +397,40 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev 
           kid[3 * kw + u] = k.d;
         }
        }
+       if (summ) {
+         // Lane l of a wave holds key (tile start + l) for each e: the
+         // chunk and the passes are tile-aligned, so a wave's 64 lanes
+         // cover one tile; keys past kend are left out of the ballots.
+#pragma unroll
+         for (int e = 0; e < kStageBatch; ++e) {
+           const int j = j0 + e * kThreads;
+           const bool valid = j < kend;
+           const uint32_t ok = valid ? okb[j - kid0] : 0u;
+           const uint64_t vm = __ballot(valid);
+           if (vm == 0) continue;
+           uint32_t an = 0xffu, orr = 0u;
+#pragma unroll
+           for (int g = 0; g < kMaxGroups; ++g) {
+             const uint64_t bm = __ballot(valid && ((ok >> g) & 1u));
+             orr |= (uint32_t)(bm != 0) << g;
+             an &= ~((uint32_t)(bm != vm) << g);
+           }
+           if (lane == 0) {
+             const int tl = (j - kid0) / BN;
+             tand[tl] = (uint8_t)an;
+             tor[tl] = (uint8_t)orr;
+             tcnt[tl] = (int16_t)__popcll(vm);
+           }
+         }
+       }
       }
       __syncthreads();
     }
     uint8_t cls = BMATTN_TILE_EMPTY;
     if (tid < tpc && bidx < t.n_kt) {
-      cls = groups     ? classify_tile_groups(m, b, qlo, bidx * BN, BM, BN, ng, rg.hi, okb, kid0)
+      cls = summ       ? classify_tile_summary(m, b, qlo, bidx * BN, BM, BN, ng, hmin, tand[tid], tor[tid],
+                                               tcnt[tid], rg.hi, okb, kid0)
+            : groups   ? classify_tile_groups(m, b, qlo, bidx * BN, BM, BN, ng, rg.hi, okb, kid0)
             : composed ? classify_tile_enum(m, b, qlo, bidx * BN, BM, BN, qid, qturn, qdoc, kid, kw, kid0)
                        : classify_tile(m, b, qlo, bidx * BN, BM, BN, qid, qmin, qmax, kid + tid * (BN + 1));
       t.tile_class[rowoff + bidx] = cls;
