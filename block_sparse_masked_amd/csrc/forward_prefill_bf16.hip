@@ -485,7 +485,8 @@ __device__ __forceinline__ void pv_product(const char* stage, const bf16x8 (&pf)
 }
 
 // One kv tile for one wave: copies of the next tile into `nxt`,
-// then the S product, softmax and P V product of tile kt from `cur`.
+// then the S product, softmax and P V product of tile kt from `cur` (`kp`:
+// the first K fragments of `cur`, read by the caller).
 template <int D, bool PAGED, bool MASKED, bool COMP>
 __device__ __forceinline__ void kv_step(const char* cur, char* nxt, bool has_next, bool mnext,
                                         int ktn, int kt, const int32_t* ahead, int& kt_ahead,
@@ -609,7 +610,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(FwdDev p) {
   }
   end_of_tile();
   // The first K fragments of the next tile are read right after each
-  // barrier, ahead of the previous tile's remaining P V MFMAs.
+  // barrier, ahead of the previous tile's remaining P V MFMAs.  (After the
+  // last tile that read is of a stage no copy fills any more; the values
+  // are never used.)
   KPre<D> kp;
   k_prefetch<D>(smem, ad, kp);
 
