@@ -1,7 +1,8 @@
 """HIP-graph capture of the hot path (block-mask build + forward), as the
-benchmark replays it: every replay, with eager work between replays, must
-reproduce the eagerly launched result bit for bit (the kernels are
-deterministic), and the eager result must match the oracle."""
+benchmark replays it, and of the backward call with its block-mask builds:
+every replay, with eager work between replays, must reproduce the eagerly
+launched result bit for bit (the kernels are deterministic), and the eager
+forward result must match the oracle."""
 
 import numpy as np
 import pytest
@@ -75,3 +76,49 @@ def test_graph_replay_matches_eager(name, paged):
     if not paged:
         exp_o, exp_l = oracle_dense(lay, q.cpu(), k.cpu(), v.cpu())
         check_close(ref_o, ref_l, exp_o, exp_l, lay.dtype, name)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kind", ["causal", "shared_prefix", "composed"])
+def test_backward_graph_replay_matches_eager(kind):
+    """The backward call with both block-mask builds it needs (the 128 x 64
+    rows and the 64 x 128 columns), captured as one graph: every replay,
+    with eager work between replays, gives the eager gradients bit for bit
+    (the backward has no atomics)."""
+    rng = np.random.default_rng(23)
+    lay = synth.random_layout(rng, kind, n_seqs=3, max_len=300, min_len=40, H=3, D=128, dtype="bf16")
+    say(f"backward graph case {kind}: seqs {lay.n_seqs} q {lay.total_q}")
+    q, k, v = synth.make_dense_qkv(lay, seed=5, device=DEV)
+    do = synth.make_dense_qkv(lay, seed=6, device=DEV)[0]
+    desc = desc_for(lay)
+    rows = bm.build_block_mask(desc, *bm.BWD_ROWS)
+    o, lse = bm.forward(q, k, v, desc, rows)
+    ctiles, cols = bm.build_backward_cols(desc)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(bm.backward_workspace_size(q, desc), 16), dtype=torch.uint8, device=DEV)
+
+    def step():
+        bm.build_block_mask(desc, *bm.BWD_ROWS, out=rows)
+        bm.build_backward_cols(desc, tiles=ctiles, out=cols)
+        bm.backward(q, k, v, o, lse, do, desc, rows, cols, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (dq, dk, dv)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        for x in (dq, dk, dv):
+            x.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        x = torch.randn(256, 256, device=DEV)
+        (x @ x).sum().item()
+        for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+            assert torch.equal(got, want), f"replay {r}: {name} differs from the eager launch"
