@@ -122,3 +122,50 @@ def test_backward_graph_replay_matches_eager(kind):
         (x @ x).sum().item()
         for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
             assert torch.equal(got, want), f"replay {r}: {name} differs from the eager launch"
+
+
+@pytest.mark.gpu
+def test_duplicated_answer_step_graph_replay_matches_eager():
+    """The duplicated-answer step as the benchmark captures it (relabel the
+    ids with the layout check, build the block mask, forward): every replay
+    reproduces the eager O and LSE bit for bit and reports a valid layout."""
+    rng = np.random.default_rng(29)
+    lay = synth.random_layout(rng, "strip_thinking_duplicated", n_seqs=2, max_len=400, min_len=100,
+                              H=2, D=128, dtype="bf16")
+    say(f"duplicated graph case: seqs {lay.n_seqs} q {lay.total_q}")
+    q, k, v = synth.make_dense_qkv(lay, seed=7, device=DEV)
+    desc = desc_for(lay)
+    tiles = bm.build_block_mask(desc, 128, 64)
+    out = torch.empty_like(q)
+    lse = torch.empty((lay.num_heads, lay.total_q), dtype=torch.float32, device=DEV)
+    holder = {}
+
+    def step():
+        holder["flags"] = bm.relabel(desc, check=True)
+        bm.build_block_mask(desc, 128, 64, out=tiles)
+        bm.forward(q, k, v, desc, tiles, out=out, lse=lse)
+
+    step()
+    torch.cuda.synchronize()
+    assert int(holder["flags"].item()) == 0, "the generated layout must meet the relabelling conditions"
+    ref_o, ref_l = out.clone(), lse.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    flags = holder["flags"]
+    for r in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        flags.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        x = torch.randn(256, 256, device=DEV)
+        (x @ x).sum().item()
+        assert int(flags.item()) == 0, f"replay {r}: layout check"
+        assert torch.equal(out, ref_o), f"replay {r}: O differs from the eager launch"
+        assert torch.equal(lse, ref_l), f"replay {r}: LSE differs from the eager launch"
