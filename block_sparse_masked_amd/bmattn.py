@@ -11,7 +11,6 @@ implementation behind these names.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from dataclasses import dataclass
 from typing import Optional
@@ -276,6 +275,10 @@ def build_block_mask(desc: MaskDesc, block_m: int, block_n: int, out: Optional[B
                      stream=None) -> BlockMask:
     """bmattn_build_block_mask: tile classes, kv-tile lists and row schedule."""
     bm = alloc_block_mask(desc, block_m, block_n, desc.cu_seqlens_q.device) if out is None else out
+    _check_desc(desc, "build_block_mask", desc.cu_seqlens_q.device)
+    _require((bm.block_m, bm.block_n) == (block_m, block_n), "build_block_mask",
+             f"out was allocated for {bm.block_m}x{bm.block_n} tiles, not {block_m}x{block_n}")
+    _check_tiles(bm, "build_block_mask", desc.cu_seqlens_q.device)
     d, t = desc.c(), bm.c()
     _check(lib().bmattn_build_block_mask(ctypes.byref(d), ctypes.byref(t), _stream(stream)),
            "bmattn_build_block_mask")
@@ -288,6 +291,104 @@ def _dtype_code(dt: torch.dtype) -> int:
     if dt == torch.float32:
         return F32
     raise BmattnError(2, "forward", f"dtype {dt} is not supported")
+
+
+def _require(ok: bool, fn: str, msg: str, status: int = 1):
+    if not ok:
+        raise BmattnError(status, fn, msg)
+
+
+def _check_tensor(t, fn: str, name: str, device, dtype=None, shape=None, inner_contig=True):
+    """One argument tensor: on ``device``, of ``dtype`` and ``shape`` (None
+    entries match any extent), its last dimension contiguous."""
+    _require(isinstance(t, torch.Tensor), fn, f"{name} must be a torch tensor")
+    _require(t.device == device, fn, f"{name} is on {t.device}, expected {device}")
+    if dtype is not None:
+        _require(t.dtype == dtype, fn, f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None:
+        _require(t.dim() == len(shape) and all(w is None or w == g for w, g in zip(shape, t.shape)),
+                 fn, f"{name} has shape {tuple(t.shape)}, expected "
+                     f"{tuple('*' if w is None else w for w in shape)}")
+    if inner_contig and t.dim() > 0 and t.numel() > 0:
+        _require(t.stride(-1) == 1, fn, f"{name} must be contiguous in its last dimension")
+
+
+def _check_desc(desc: MaskDesc, fn: str, device):
+    """The description's device arrays: on ``device``, int32, of the lengths
+    its sizes give."""
+    n, tq, tk = desc.n_seqs, desc.total_q, desc.total_k
+    for name, length in (("cu_seqlens_q", n + 1), ("cu_seqlens_k", n + 1), ("seg_q", tq),
+                         ("seg_k", tk), ("role_k", tk), ("turn_q", tq), ("turn_k", tk),
+                         ("doc_q", tq), ("doc_k", tk)):
+        t = getattr(desc, name)
+        if t is not None:
+            _check_tensor(t, fn, f"desc.{name}", device, torch.int32, (length,))
+            _require(t.is_contiguous(), fn, f"desc.{name} must be contiguous")
+
+
+def _check_tiles(tiles, fn: str, device, row_major: bool = True):
+    """A block mask's arrays (or column lists'): on ``device``, int32 (classes
+    uint8), with as many elements as its shape needs."""
+    if row_major:
+        rows = tiles.n_seqs * tiles.n_qt
+        arrays = (("tile_class", torch.uint8, rows * tiles.n_kt), ("full_cnt", torch.int32, rows),
+                  ("part_cnt", torch.int32, rows), ("full_idx", torch.int32, rows * tiles.n_kt),
+                  ("part_idx", torch.int32, rows * tiles.n_kt), ("row_order", torch.int32, rows))
+    else:
+        cols = tiles.n_seqs * tiles.n_kt
+        arrays = (("full_cnt", torch.int32, cols), ("part_cnt", torch.int32, cols),
+                  ("full_idx", torch.int32, cols * tiles.n_qt),
+                  ("part_idx", torch.int32, cols * tiles.n_qt), ("col_order", torch.int32, cols))
+    for name, dt, numel in arrays:
+        t = getattr(tiles, name)
+        _check_tensor(t, fn, f"tiles.{name}", device, dt)
+        _require(t.is_contiguous() and t.numel() >= numel, fn,
+                 f"tiles.{name} must be contiguous with at least {numel} elements")
+
+
+def _check_fwd(q, k, v, o, lse, desc: MaskDesc, tiles, block_table, workspace, fn="forward"):
+    """Everything the C ABI cannot see: devices, dtypes, extents and the
+    contiguous head_dim of every tensor argument of bmattn_forward."""
+    _check_tensor(q, fn, "q", q.device, None, (desc.total_q, None, None))
+    dev, dt = q.device, q.dtype
+    H, D = q.shape[1], q.shape[2]
+    _check_tensor(o, fn, "out", dev, dt, (desc.total_q, H, D))
+    if block_table is None:
+        for name, t in (("k", k), ("v", v)):
+            _check_tensor(t, fn, name, dev, dt, (desc.total_k, H, D))
+    else:
+        _check_tensor(k, fn, "k pool", dev, dt, (None, None, H, D))
+        _check_tensor(v, fn, "v pool", dev, dt, tuple(k.shape))
+        _check_tensor(block_table, fn, "block_table", dev, torch.int32, (None, None))
+        _require(block_table.shape[0] >= desc.n_seqs, fn,
+                 f"block_table has {block_table.shape[0]} rows for {desc.n_seqs} sequences")
+    if lse is not None:
+        _check_tensor(lse, fn, "lse", dev, torch.float32, (H, desc.total_q))
+    if workspace is not None:
+        _check_tensor(workspace, fn, "workspace", dev)
+        _require(workspace.is_contiguous(), fn, "workspace must be contiguous")
+    _check_desc(desc, fn, dev)
+    if tiles is not None:
+        _check_tiles(tiles, fn, dev)
+
+
+def _check_bwd(q, k, v, o, lse, do, dq, dk, dv, desc: MaskDesc, rows, cols, workspace,
+               fn="backward"):
+    """Devices, dtypes and extents of every tensor argument of bmattn_backward."""
+    _check_tensor(q, fn, "q", q.device, None, (desc.total_q, None, None))
+    dev, dt = q.device, q.dtype
+    H, D = q.shape[1], q.shape[2]
+    for name, t in (("o", o), ("do", do), ("dq", dq)):
+        _check_tensor(t, fn, name, dev, dt, (desc.total_q, H, D))
+    for name, t in (("k", k), ("v", v), ("dk", dk), ("dv", dv)):
+        _check_tensor(t, fn, name, dev, dt, (desc.total_k, H, D))
+    _check_tensor(lse, fn, "lse", dev, torch.float32, (H, desc.total_q))
+    if workspace is not None:
+        _check_tensor(workspace, fn, "workspace", dev)
+        _require(workspace.is_contiguous(), fn, "workspace must be contiguous")
+    _check_desc(desc, fn, dev)
+    _check_tiles(rows, fn, dev)
+    _check_tiles(cols, fn, dev, row_major=False)
 
 
 def _fwd_args(q, k, v, o, lse, *, block_table=None, page_size=0, scale=0.0, workspace=None):
@@ -313,6 +414,7 @@ def _fwd_args(q, k, v, o, lse, *, block_table=None, page_size=0, scale=0.0, work
 
 def forward_workspace_size(q, k, v, desc: MaskDesc, tiles: BlockMask, *, block_table=None) -> int:
     o = q  # only shapes and strides are read
+    _check_fwd(q, k, v, o, None, desc, tiles, block_table, None, "forward_workspace_size")
     a = _fwd_args(q, k, v, o, None, block_table=block_table)
     n = ctypes.c_size_t()
     d, t = desc.c(), tiles.c()
@@ -326,10 +428,12 @@ def forward(q, k, v, desc: MaskDesc, tiles: BlockMask, *, block_table=None, scal
     """bmattn_forward.  q [total_q, H, D]; k, v [total_k, H, D] or page pools
     [num_pages, page_size, H, D] with ``block_table`` [n_seqs, pages] int32.
     Returns (O, LSE) with O like q and LSE fp32 [H, total_q]."""
+    _require(isinstance(q, torch.Tensor) and q.is_cuda, "forward", "q must be a device (cuda) tensor")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and with_lse:
         lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    _check_fwd(q, k, v, out, lse, desc, tiles, block_table, workspace)
     if workspace is None:
         need = forward_workspace_size(q, k, v, desc, tiles, block_table=block_table)
         if need:
@@ -343,6 +447,13 @@ def forward(q, k, v, desc: MaskDesc, tiles: BlockMask, *, block_table=None, scal
 
 def paged_gather(pool, block_table, desc: MaskDesc, stream=None):
     """bmattn_paged_gather: pool [num_pages, page_size, H, D] -> [total_k, H, D]."""
+    _check_tensor(pool, "paged_gather", "pool", pool.device, None, (None, None, None, None))
+    _require(pool.dtype in (torch.bfloat16, torch.float32), "paged_gather",
+             f"pool dtype {pool.dtype} is not supported", 2)
+    _check_tensor(block_table, "paged_gather", "block_table", pool.device, torch.int32, (None, None))
+    _require(block_table.shape[0] >= desc.n_seqs, "paged_gather",
+             f"block_table has {block_table.shape[0]} rows for {desc.n_seqs} sequences")
+    _check_desc(desc, "paged_gather", pool.device)
     n_pages, ps, H, D = pool.shape
     out = torch.empty((desc.total_k, H, D), dtype=pool.dtype, device=pool.device)
     d = desc.c()
@@ -355,8 +466,11 @@ def paged_gather(pool, block_table, desc: MaskDesc, stream=None):
 
 def debug_dense_mask(desc: MaskDesc, tiles: BlockMask, seq: int, stream=None):
     """bmattn_debug_dense_mask: uint8 [n_qt*block_m, n_kt*block_n] of one sequence."""
+    dev = tiles.tile_class.device
+    _check_desc(desc, "debug_dense_mask", dev)
+    _check_tiles(tiles, "debug_dense_mask", dev)
     rows, cols = tiles.n_qt * tiles.block_m, tiles.n_kt * tiles.block_n
-    out = torch.empty((rows, cols), dtype=torch.uint8, device=tiles.tile_class.device)
+    out = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
     d, t = desc.c(), tiles.c()
     _check(lib().bmattn_debug_dense_mask(ctypes.byref(d), ctypes.byref(t), int(seq), _ptr(out), cols,
                                          _stream(stream)), "bmattn_debug_dense_mask")
@@ -366,7 +480,13 @@ def debug_dense_mask(desc: MaskDesc, tiles: BlockMask, seq: int, stream=None):
 def validate(desc: MaskDesc, block_table=None, page_size: int = 0, num_pages: int = 0,
              stream=None) -> int:
     """bmattn_validate: returns the flag word (0 = valid); synchronises."""
-    flags = torch.zeros(1, dtype=torch.int32, device=desc.cu_seqlens_q.device)
+    dev = desc.cu_seqlens_q.device
+    _check_desc(desc, "validate", dev)
+    if block_table is not None:
+        _check_tensor(block_table, "validate", "block_table", dev, torch.int32, (None, None))
+        _require(block_table.shape[0] >= desc.n_seqs, "validate",
+                 f"block_table has {block_table.shape[0]} rows for {desc.n_seqs} sequences")
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
     d = desc.c()
     _check(lib().bmattn_validate(ctypes.byref(d), _ptr(block_table),
                                  0 if block_table is None else block_table.stride(0),
@@ -406,6 +526,8 @@ def transpose_block_mask(tiles: BlockMask, out: Optional[BlockMaskCols] = None,
                             torch.empty(cols, **i32), torch.empty(cols, **i32),
                             torch.empty(cols * tiles.n_qt, **i32), torch.empty(cols * tiles.n_qt, **i32),
                             torch.empty(cols, **i32))
+    _check_tiles(tiles, "transpose_block_mask", tiles.tile_class.device)
+    _check_tiles(out, "transpose_block_mask", tiles.tile_class.device, row_major=False)
     t, c = tiles.c(), out.c()
     _check(lib().bmattn_transpose_block_mask(ctypes.byref(t), ctypes.byref(c), _stream(stream)),
            "bmattn_transpose_block_mask")
@@ -449,9 +571,11 @@ def backward(q, k, v, o, lse, do, desc: MaskDesc, rows: BlockMask, cols: BlockMa
     """bmattn_backward: (dQ, dK, dV) like q, k, v.  ``rows`` is the forward's
     128 x 64 block mask, ``cols`` the column lists of the 64 x 128 one
     (build_backward_cols)."""
+    _require(isinstance(q, torch.Tensor) and q.is_cuda, "backward", "q must be a device (cuda) tensor")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _check_bwd(q, k, v, o, lse, do, dq, dk, dv, desc, rows, cols, workspace)
     if workspace is None:
         need = backward_workspace_size(q, desc)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -476,6 +600,10 @@ def duplicated_answer_ids(desc: MaskDesc, role_q: torch.Tensor, *, loss_role: in
                        desc.total_k, desc.cu_seqlens_q, desc.cu_seqlens_k, None, None,
                        torch.empty_like(desc.role_k), torch.empty_like(desc.turn_q), desc.turn_k,
                        desc.think_role, (desc, role_q, int(loss_role), int(history_role)))
+    dev = desc.cu_seqlens_q.device
+    _check_desc(desc, "duplicated_answer_ids", dev)
+    _check_tensor(role_q, "duplicated_answer_ids", "role_q", dev, torch.int32, (desc.total_q,))
+    _check_desc(out, "duplicated_answer_ids", dev)
     flags = torch.empty(1, dtype=torch.int32, device=role_q.device) if check else None
     d = desc.c()
     _check(lib().bmattn_duplicated_answer_ids(ctypes.byref(d), _ptr(role_q), int(loss_role),
@@ -492,6 +620,3 @@ def relabel(desc: MaskDesc, check: bool = False, stream=None):
     return duplicated_answer_ids(src, role_q, loss_role=loss_role, history_role=history_role,
                                  out=desc, check=check, stream=stream)[1]
 
-
-def default_scale(head_dim: int) -> float:
-    return 1.0 / math.sqrt(head_dim)

@@ -133,6 +133,15 @@ int check_tiles(const bmattn_mask_desc* d, const bmattn_block_mask* t, bool need
   return BMATTN_OK;
 }
 
+// A launch puts one workgroup on each (tile row or column, head); the grid
+// must fit the 32-bit dispatch size.
+int check_grid(int64_t units, int32_t heads, const char* what) {
+  if (units * (int64_t)heads > (int64_t)INT32_MAX)
+    return fail(BMATTN_EUNSUPPORTED, "%s grid of %lld tile rows x %d heads exceeds 2^31 - 1 workgroups",
+                what, (long long)units, heads);
+  return BMATTN_OK;
+}
+
 TilesDev tiles_dev(const bmattn_mask_desc* d, const bmattn_block_mask* t) {
   TilesDev x{};
   x.block_m = t->block_m;
@@ -205,7 +214,7 @@ int check_fwd(const bmattn_fwd_args* a, const bmattn_mask_desc* d, const bmattn_
     return fail(BMATTN_EINVAL, "lse_stride_head must be >= total_q");
   if (!(std::isfinite(a->scale)) || a->scale < 0.f)
     return fail(BMATTN_EINVAL, "scale must be finite and >= 0 (0 selects 1/sqrt(head_dim))");
-  return BMATTN_OK;
+  return check_grid((int64_t)t->n_seqs * t->n_qt, a->num_heads, "forward");
 }
 
 int check_cols(const bmattn_block_mask* t, const bmattn_block_mask_cols* c) {
@@ -439,6 +448,10 @@ int bmattn_backward(const bmattn_bwd_args* a, const bmattn_mask_desc* desc,
   if (cols->full_cnt == nullptr || cols->part_cnt == nullptr || cols->full_idx == nullptr ||
       cols->part_idx == nullptr || cols->col_order == nullptr)
     return fail(BMATTN_EINVAL, "column list array is NULL");
+  rc = check_grid((int64_t)rows->n_seqs * rows->n_qt, a->num_heads, "backward dQ");
+  if (rc) return rc;
+  rc = check_grid((int64_t)cols->n_seqs * cols->n_kt, a->num_heads, "backward dK/dV");
+  if (rc) return rc;
   const size_t need = bwd_workspace(a, desc);
   if (need > 0 && (a->workspace == nullptr || a->workspace_bytes < need))
     return fail(BMATTN_EWORKSPACE, "the backward needs a workspace of %zu bytes (got %zu)", need,

@@ -537,22 +537,22 @@ template <int D>
 hipError_t launch_d(const BwdDev& p, hipStream_t st) {
   static_assert(2 * 2 * Lay<D>::kStage <= 160 * 1024, "two workgroups' LDS stages exceed 160 KiB");
   const int64_t rows = p.mask.total_q * p.num_heads;
+  const int64_t prep_grid = (rows * (D / 8) + kThreads - 1) / kThreads;
+  const int64_t cols = (int64_t)p.mask.n_seqs * p.c_n_kt * p.num_heads;
+  const int64_t qrows = (int64_t)p.mask.n_seqs * p.n_qt * p.num_heads;
+  if (prep_grid > INT32_MAX || cols > INT32_MAX || qrows > INT32_MAX) return hipErrorInvalidValue;
   if (rows > 0) {
-    const int64_t threads = rows * (D / 8);
-    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((uint32_t)((threads + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((uint32_t)prep_grid), dim3(kThreads), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const uint32_t cols = (uint32_t)p.mask.n_seqs * p.c_n_kt * (uint32_t)p.num_heads;
   if (cols > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(cols), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((uint32_t)cols), dim3(kThreads), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const uint32_t qrows = (uint32_t)p.mask.n_seqs * p.n_qt * (uint32_t)p.num_heads;
   if (qrows > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(qrows), dim3(kThreads), 0, st, p);
+    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((uint32_t)qrows), dim3(kThreads), 0, st, p);
     return hipGetLastError();
   }
   return hipSuccess;

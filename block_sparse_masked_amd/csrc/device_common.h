@@ -175,14 +175,4 @@ __device__ __forceinline__ int64_t paged_row(const int32_t* block_table, int64_t
                      page_shift, num_pages);
 }
 
-// Workgroups are dispatched round-robin over the 8 XCDs of the chip.  This
-// maps the dispatch index to a logical index so that consecutive logical
-// indices run on the same XCD (and share its L2), in dispatch order.
-__device__ __forceinline__ uint32_t xcd_remap(uint32_t w, uint32_t n) {
-  constexpr uint32_t kXcd = 8;
-  uint32_t xcd = w % kXcd, local = w / kXcd;
-  uint32_t per = n / kXcd, rem = n % kXcd;
-  return xcd * per + (xcd < rem ? xcd : rem) + local;
-}
-
 }  // namespace bmattn

@@ -669,13 +669,13 @@ constexpr int kv_groups() {
 template <typename T, int D>
 hipError_t launch_typed(const FwdDev& p, bool paged, hipStream_t st) {
   constexpr int KG = kv_groups<T, D>();
-  const uint32_t n_rows = (uint32_t)p.mask.n_seqs * p.n_qt;
-  const uint32_t grid = n_rows * (uint32_t)p.num_heads;
+  const int64_t grid = (int64_t)p.mask.n_seqs * p.n_qt * p.num_heads;
   if (grid == 0) return hipSuccess;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
   if (paged) {
-    hipLaunchKernelGGL((prefill_kernel<T, D, true, KG>), dim3(grid), dim3(kThreads * KG), 0, st, p);
+    hipLaunchKernelGGL((prefill_kernel<T, D, true, KG>), dim3((uint32_t)grid), dim3(kThreads * KG), 0, st, p);
   } else {
-    hipLaunchKernelGGL((prefill_kernel<T, D, false, KG>), dim3(grid), dim3(kThreads * KG), 0, st, p);
+    hipLaunchKernelGGL((prefill_kernel<T, D, false, KG>), dim3((uint32_t)grid), dim3(kThreads * KG), 0, st, p);
   }
   return hipGetLastError();
 }

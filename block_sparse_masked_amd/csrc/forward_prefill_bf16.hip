@@ -667,9 +667,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(FwdDev p) {
 template <int D>
 hipError_t launch_d(const FwdDev& p, bool paged, hipStream_t st) {
   static_assert(2 * 2 * Lay<D>::kStage <= 160 * 1024, "two workgroups' LDS stages exceed 160 KiB");
-  const uint32_t n_rows = (uint32_t)p.mask.n_seqs * p.n_qt;
-  const uint32_t grid = n_rows * (uint32_t)p.num_heads;
-  if (grid == 0) return hipSuccess;
+  const int64_t grid64 = (int64_t)p.mask.n_seqs * p.n_qt * p.num_heads;
+  if (grid64 == 0) return hipSuccess;
+  if (grid64 > INT32_MAX) return hipErrorInvalidValue;
+  const uint32_t grid = (uint32_t)grid64;
   const bool comp = p.mask.kind == BMATTN_MASK_COMPOSED;
   if (paged && comp) {
     hipLaunchKernelGGL((prefill_bf16_kernel<D, true, true>), dim3(grid), dim3(kThreads), 0, st, p);

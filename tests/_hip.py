@@ -103,3 +103,65 @@ def run_dense(layout, seed=0, BM=128, BN=64, scale=0.0):
 
 def oracle_dense(layout, q, k, v, scale=None):
     return oforward.forward(layout, q, k, v, scale=scale)
+
+
+def oracle_workers() -> int:
+    """Host threads for the oracle: the cores this process may use, at most 16."""
+    import os
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def oracle_one_sequence(layout, q, k, v, heads=None, scale=None):
+    """O [T, H, D] and LSE [H, T] (float64) of a one-sequence contiguous layout,
+    every head (or ``heads``): the oracle's dense mask, built once, and its
+    three passes per head, the heads spread over host threads with BLAS
+    single-threaded in each (numpy releases the interpreter lock in BLAS and
+    in its array loops)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    from oracle import attention as oattention
+
+    assert layout.n_seqs == 1 and not layout.paged
+    H, T = layout.num_heads, layout.total_q
+    heads = list(range(H)) if heads is None else list(heads)
+    sc = oattention.default_scale(layout.head_dim) if not scale else scale
+    vis = omasks.visible_for_layout(layout, 0)
+    O = np.zeros((T, H, layout.head_dim), np.float64)
+    L = np.full((H, T), -np.inf, np.float64)
+
+    def one(h):
+        O[:, h], L[h] = oattention.three_pass(oforward.head_slice(q, h), oforward.head_slice(k, h),
+                                              oforward.head_slice(v, h), vis, sc)
+
+    with threadpool_limits(1), ThreadPoolExecutor(oracle_workers()) as ex:
+        list(ex.map(one, heads))
+    return O, L
+
+
+def oracle_backward_one_sequence(layout, q, k, v, do, heads, workers=2):
+    """(dQ, dK, dV) [T, len(heads), D] float64 of a one-sequence contiguous
+    layout for the listed heads: the oracle's dense mask, built once, and
+    its per-sequence backward per head, ``workers`` heads at a time (each
+    holds several T x T float64 matrices) with the BLAS threads shared out."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    from oracle import attention as oattention
+    from oracle import backward as obackward
+
+    assert layout.n_seqs == 1 and not layout.paged
+    heads = list(heads)
+    sc = oattention.default_scale(layout.head_dim)
+    vis = omasks.visible_for_layout(layout, 0)
+    T, D = layout.total_q, layout.head_dim
+    out = [np.zeros((T, len(heads), D), np.float64) for _ in range(3)]
+
+    def one(i):
+        h = heads[i]
+        g = obackward.sequence_backward(*(oforward.head_slice(x, h) for x in (q, k, v)), vis, sc,
+                                        oforward.head_slice(do, h))
+        for a, b in zip(out, g):
+            a[:, i] = b
+
+    with threadpool_limits(max(1, oracle_workers() // workers)), ThreadPoolExecutor(workers) as ex:
+        list(ex.map(one, range(len(heads))))
+    return out

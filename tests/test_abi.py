@@ -257,3 +257,106 @@ def test_struct_layouts_match_the_header(tmp_path):
         assert int(out[cname]) == ctypes.sizeof(cls), cname
         for f in fields:
             assert int(out[f"{cname}.{f}"]) == getattr(cls, f).offset, (cname, f)
+
+
+def test_forward_grid_beyond_int32_rejected():
+    # 2 sequences x ceil(2^30 / 128) query tiles x 256 heads is more than
+    # 2^31 - 1 workgroups: refused on the host, never launched short.
+    L = bm.lib()
+    d = _desc(mq=1 << 30, mk=100)
+    t = _tiles(d)
+    a = _args(num_heads=256)
+    assert L.bmattn_forward(ctypes.byref(a), ctypes.byref(d), ctypes.byref(t), None) == 2
+    assert b"grid" in L.bmattn_last_error()
+    a = _args(num_heads=1)
+    assert L.bmattn_forward_workspace_size(ctypes.byref(a), ctypes.byref(d), ctypes.byref(t),
+                                           ctypes.byref(ctypes.c_size_t())) == 0
+
+
+# ---- the binding's tensor checks (CPU tensors; no library call is reached) --
+
+def _cpu_case(paged=False, T=40, H=2, D=64):
+    import torch
+    import synth
+    lay = synth.Layout("t", "causal", "bf16", H, D, [T], [T])
+    desc = bm.MaskDesc.create("causal", lay.cu_q, lay.cu_k, T, T, device="cpu")
+    q = torch.zeros(T, H, D, dtype=torch.bfloat16)
+    if paged:
+        k = torch.zeros(4, 16, H, D, dtype=torch.bfloat16)
+        bt = torch.zeros(1, 3, dtype=torch.int32)
+    else:
+        k, bt = torch.zeros(T, H, D, dtype=torch.bfloat16), None
+    lse = torch.zeros(H, T, dtype=torch.float32)
+    return desc, q, k, k.clone(), q.clone(), lse, bt
+
+
+@pytest.mark.parametrize("bad", ["kshape", "vdtype", "oshape", "lse_dtype", "lse_shape",
+                                 "q_inner_stride", "ktokens"])
+def test_binding_rejects_bad_tensors(bad):
+    import torch
+    desc, q, k, v, o, lse, bt = _cpu_case()
+    if bad == "kshape":
+        k = torch.zeros(40, 1, 64, dtype=torch.bfloat16)  # fewer heads than q (GQA shape)
+    elif bad == "vdtype":
+        v = v.float()
+    elif bad == "oshape":
+        o = o[:20]
+    elif bad == "lse_dtype":
+        lse = lse.double()
+    elif bad == "lse_shape":
+        lse = lse[:, :10]
+    elif bad == "q_inner_stride":
+        q = torch.zeros(40, 2, 128, dtype=torch.bfloat16)[:, :, ::2]
+    elif bad == "ktokens":
+        k = k[:30]
+    with pytest.raises(bm.BmattnError) as e:
+        bm._check_fwd(q, k, v, o, lse, desc, None, None, None)
+    assert e.value.status == 1
+
+
+@pytest.mark.parametrize("bad", ["int64_table", "short_table", "pool_rank", "vpool_shape"])
+def test_binding_rejects_bad_paged_tensors(bad):
+    import torch
+    desc, q, k, v, o, lse, bt = _cpu_case(paged=True)
+    if bad == "int64_table":
+        bt = bt.long()  # torch.tensor's default integer type; the kernels read int32
+    elif bad == "short_table":
+        bt = torch.zeros(0, 3, dtype=torch.int32)
+    elif bad == "pool_rank":
+        k = k.reshape(64, 2, 64)
+    elif bad == "vpool_shape":
+        v = torch.zeros(3, 16, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(bm.BmattnError) as e:
+        bm._check_fwd(q, k, v, o, lse, desc, None, bt, None)
+    assert e.value.status == 1
+
+
+def test_binding_accepts_consistent_tensors():
+    for paged in (False, True):
+        desc, q, k, v, o, lse, bt = _cpu_case(paged=paged)
+        bm._check_fwd(q, k, v, o, lse, desc, None, bt, None)
+
+
+@pytest.mark.parametrize("bad", ["dk_shape", "do_dtype", "lse_shape"])
+def test_binding_rejects_bad_backward_tensors(bad):
+    import torch
+    desc, q, k, v, o, lse, _ = _cpu_case()
+    do, dq, dk, dv = q.clone(), q.clone(), k.clone(), v.clone()
+    if bad == "dk_shape":
+        dk = dk[:10]
+    elif bad == "do_dtype":
+        do = do.float()
+    elif bad == "lse_shape":
+        lse = lse[:1]
+    with pytest.raises(bm.BmattnError) as e:
+        bm._check_bwd(q, k, v, o, lse, do, dq, dk, dv, desc, None, None, None)
+    assert e.value.status == 1
+
+
+def test_binding_rejects_wrong_id_lengths():
+    import torch
+    lay_cu = [0, 40]
+    d = bm.MaskDesc.create("shared_prefix", lay_cu, lay_cu, 40, 40, device="cpu",
+                           seg_q=[0] * 40, seg_k=[0] * 39)
+    with pytest.raises(bm.BmattnError):
+        bm._check_desc(d, "forward", torch.device("cpu"))

@@ -236,3 +236,25 @@ def test_composed_single_terms_match_plain_kinds_bit_exact():
         torch.cuda.synchronize()
         for f in ("tile_class", "full_cnt", "part_cnt", "full_idx", "part_idx", "row_order"):
             assert torch.equal(getattr(a, f), getattr(b, f)), (kind, f)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("kind", ["causal", "full"])
+@pytest.mark.parametrize("BM,BN", [(128, 64), (1, 64)])
+@pytest.mark.parametrize("layout", ["many_rows", "many_tiles"])
+def test_tiles_general_classifier_causal_and_full(kind, BM, BN, layout):
+    # CAUSAL and FULL masks of more than 1024 tile rows (1100 short
+    # sequences) or more than 65 536 tiles (one sequence of 33 000 tokens)
+    # take the general classifier, not the one-workgroup path of small masks.
+    if layout == "many_rows":
+        rng = np.random.default_rng(11 + BM + len(kind))
+        lens = [int(x) for x in rng.integers(1, 300, size=1100)]
+    else:
+        lens = [33000]
+    lay = synth.Layout(layout, kind, "bf16", 1, 128, lens, lens)
+    n_qt, n_kt = -(-max(lens) // BM), -(-max(lens) // BN)
+    rows = len(lens) * n_qt
+    assert rows > 1024 or rows * n_kt > 65536
+    desc = _hip.desc_for(lay)
+    say(f"general classifier kind={kind} {layout} BM={BM} BN={BN} rows={rows} tiles={rows * n_kt}")
+    _hip.check_tiles(lay, desc, BM, BN)
