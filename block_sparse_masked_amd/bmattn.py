@@ -29,7 +29,7 @@ TILE_EMPTY, TILE_PARTIAL, TILE_FULL = 0, 1, 2
 STATUS = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "EALIGN", 4: "EHIP", 5: "EWORKSPACE"}
 
 EXPORTS = ("bmattn_block_mask_shape", "bmattn_build_block_mask", "bmattn_forward_workspace_size",
-           "bmattn_forward", "bmattn_paged_gather", "bmattn_debug_dense_mask", "bmattn_validate",
+           "bmattn_forward", "bmattn_forward_noalloc", "bmattn_paged_gather", "bmattn_debug_dense_mask", "bmattn_validate",
            "bmattn_duplicated_answer_ids", "bmattn_transpose_block_mask",
            "bmattn_backward_workspace_size", "bmattn_backward", "bmattn_status_string",
            "bmattn_last_error", "bmattn_abi_version")
@@ -120,6 +120,8 @@ def lib():
                                                     ctypes.POINTER(ctypes.c_size_t)]
         L.bmattn_forward.argtypes = [ctypes.POINTER(FwdArgsC), ctypes.POINTER(MaskDescC),
                                      ctypes.POINTER(BlockMaskC), _p]
+        L.bmattn_forward_noalloc.argtypes = [ctypes.POINTER(FwdArgsC), ctypes.POINTER(MaskDescC),
+                                             ctypes.POINTER(BlockMaskC), _p]
         L.bmattn_paged_gather.argtypes = [_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_int64, _p, ctypes.c_int64,
@@ -442,6 +444,29 @@ def forward(q, k, v, desc: MaskDesc, tiles: BlockMask, *, block_table=None, scal
     d, t = desc.c(), tiles.c()
     _check(lib().bmattn_forward(ctypes.byref(a), ctypes.byref(d), ctypes.byref(t), _stream(stream)),
            "bmattn_forward")
+    return out, lse
+
+
+NOALLOC_MAX_WORKSPACE = 96 << 20  # BMATTN_NOALLOC_MAX_WORKSPACE
+
+
+def forward_noalloc(q, k, v, desc: MaskDesc, tiles: BlockMask, *, block_table=None,
+                    scale: float = 0.0, out=None, lse=None, stream=None):
+    """bmattn_forward_noalloc: the forward with the decode split workspace
+    taken from the library's static scratch (the library allocates nothing;
+    this binding allocates ``out`` / ``lse`` only when they are not given).
+    Calls that overlap in time on one GPU race on that scratch."""
+    _require(isinstance(q, torch.Tensor) and q.is_cuda, "forward_noalloc",
+             "q must be a device (cuda) tensor")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    _check_fwd(q, k, v, out, lse, desc, tiles, block_table, None, "forward_noalloc")
+    a = _fwd_args(q, k, v, out, lse, block_table=block_table, scale=scale, workspace=None)
+    d, t = desc.c(), tiles.c()
+    _check(lib().bmattn_forward_noalloc(ctypes.byref(a), ctypes.byref(d), ctypes.byref(t),
+                                        _stream(stream)), "bmattn_forward_noalloc")
     return out, lse
 
 

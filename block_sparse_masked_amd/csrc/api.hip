@@ -334,8 +334,14 @@ int bmattn_forward_workspace_size(const bmattn_fwd_args* args, const bmattn_mask
   return BMATTN_OK;
 }
 
-int bmattn_forward(const bmattn_fwd_args* a, const bmattn_mask_desc* desc,
-                   const bmattn_block_mask* t, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward of both entry points: `noalloc` takes the decode split
+// workspace from the library's static scratch instead of args->workspace.
+int forward_run(const bmattn_fwd_args* a, const bmattn_mask_desc* desc, const bmattn_block_mask* t,
+                void* stream, bool noalloc) {
   int rc = check_fwd(a, desc, t);
   if (rc) return rc;
   const Path path = path_of(t);
@@ -378,13 +384,38 @@ int bmattn_forward(const bmattn_fwd_args* a, const bmattn_mask_desc* desc,
   const bool paged = a->block_table != nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
+  if (noalloc && a->workspace != nullptr)
+    return fail(BMATTN_EINVAL, "bmattn_forward_noalloc takes no workspace (it uses the library's "
+                               "static scratch): pass workspace = NULL");
   if (path == Path::kDecode) {
     const size_t need = decode_workspace(a, t);
-    if (a->workspace == nullptr || a->workspace_bytes < need)
-      return fail(BMATTN_EWORKSPACE, "decode needs a workspace of %zu bytes (got %zu)", need,
-                  a->workspace == nullptr ? (size_t)0 : a->workspace_bytes);
-    if (!aligned16(a->workspace)) return fail(BMATTN_EALIGN, "workspace must be 16-byte aligned");
-    p.ws = static_cast<float*>(a->workspace);
+    if (noalloc) {
+      if (need > decode_scratch_bytes())
+        return fail(BMATTN_EWORKSPACE,
+                    "this decode needs %zu bytes of split workspace; the static scratch of "
+                    "bmattn_forward_noalloc holds %zu (use bmattn_forward with a workspace)",
+                    need, decode_scratch_bytes());
+      if (st != nullptr) {
+        int sdev = -1, cdev = -1;
+        hipError_t e2 = hipStreamGetDevice(st, &sdev);
+        if (e2 != hipSuccess) return hip_fail(e2, "hipStreamGetDevice");
+        e2 = hipGetDevice(&cdev);
+        if (e2 != hipSuccess) return hip_fail(e2, "hipGetDevice");
+        if (sdev != cdev)
+          return fail(BMATTN_EINVAL, "the stream's device (%d) is not the current device (%d)",
+                      sdev, cdev);
+      }
+      void* ws = nullptr;
+      hipError_t e2 = decode_scratch(&ws);
+      if (e2 != hipSuccess) return hip_fail(e2, "static scratch address");
+      p.ws = static_cast<float*>(ws);
+    } else {
+      if (a->workspace == nullptr || a->workspace_bytes < need)
+        return fail(BMATTN_EWORKSPACE, "decode needs a workspace of %zu bytes (got %zu)", need,
+                    a->workspace == nullptr ? (size_t)0 : a->workspace_bytes);
+      if (!aligned16(a->workspace)) return fail(BMATTN_EALIGN, "workspace must be 16-byte aligned");
+      p.ws = static_cast<float*>(a->workspace);
+    }
     p.split_tiles = kDecodeSplitTiles;
     p.n_splits = (int32_t)cdiv(t->n_kt, kDecodeSplitTiles);
     e = launch_forward_decode(p, a->dtype, paged, st);
@@ -393,6 +424,20 @@ int bmattn_forward(const bmattn_fwd_args* a, const bmattn_mask_desc* desc,
   }
   if (e != hipSuccess) return hip_fail(e, "bmattn_forward launch");
   return BMATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bmattn_forward(const bmattn_fwd_args* a, const bmattn_mask_desc* desc,
+                   const bmattn_block_mask* t, void* stream) {
+  return forward_run(a, desc, t, stream, false);
+}
+
+int bmattn_forward_noalloc(const bmattn_fwd_args* a, const bmattn_mask_desc* desc,
+                           const bmattn_block_mask* t, void* stream) {
+  return forward_run(a, desc, t, stream, true);
 }
 
 int bmattn_transpose_block_mask(const bmattn_block_mask* tiles, const bmattn_block_mask_cols* out,

@@ -20,11 +20,22 @@
 //    order (deterministic), O = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 
 namespace bmattn {
 namespace {
+
+// The split workspace of bmattn_forward_noalloc: a file-scope device array
+// that every call on a GPU shares (each GPU holds its own copy until the
+// process ends).  Host code never passes `scratch` itself to a kernel (on
+// the host it names a stand-in, not device memory): decode_scratch() looks
+// up the array's device address once per device and hands that out.
+constexpr size_t kScratchBytes = BMATTN_NOALLOC_MAX_WORKSPACE;
+static __device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
 
 constexpr int kBN = 64;
 constexpr int kThreads = 256;
@@ -337,6 +348,26 @@ hipError_t launch_typed(const FwdDev& p, bool paged, hipStream_t st) {
 }
 
 }  // namespace
+
+size_t decode_scratch_bytes() { return kScratchBytes; }
+
+hipError_t decode_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_forward_decode(const FwdDev& p, int dtype, bool paged, hipStream_t st) {
   if (p.block_m != 1 || p.block_n != kBN) return hipErrorInvalidValue;

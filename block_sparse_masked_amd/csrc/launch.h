@@ -128,4 +128,10 @@ hipError_t launch_forward_prefill(const FwdDev& p, int dtype, bool paged, hipStr
 hipError_t launch_forward_prefill_bf16(const FwdDev& p, bool paged, hipStream_t st);
 hipError_t launch_forward_decode(const FwdDev& p, int dtype, bool paged, hipStream_t st);
 
+// The static split workspace of the entry point that allocates nothing: its
+// size in bytes, and its device address on the calling thread's current
+// device (looked up once per device).
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void** ptr);
+
 }  // namespace bmattn

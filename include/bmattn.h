@@ -6,8 +6,9 @@
  * caller; device buffers are plain HIP device allocations.  Every call is
  * asynchronous on the stream it is given (a hipStream_t passed as void*;
  * NULL means the default stream).  The library allocates no memory and keeps
- * no state between calls beyond its loaded code objects, so calls from
- * different host threads are safe when they touch disjoint output buffers.
+ * no state between calls beyond its loaded code objects (and the static
+ * device array of bmattn_forward_noalloc, below), so calls from different
+ * host threads are safe when they touch disjoint output buffers.
  *
  * Error behaviour: every entry point returns a bmattn_status.  Arguments are
  * validated on the host before anything is launched; an invalid or
@@ -231,6 +232,27 @@ int bmattn_forward_workspace_size(const bmattn_fwd_args* args, const bmattn_mask
  * with one of the compiled tile shapes. */
 int bmattn_forward(const bmattn_fwd_args* args, const bmattn_mask_desc* desc,
                    const bmattn_block_mask* tiles, void* stream);
+
+/* ---- forward without any allocation -----------------------------------------
+ * For callers that cannot allocate device memory at call time: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same computation and kernels as bmattn_forward (bit-identical
+ * results), but the decode path's split workspace is a static device array
+ * of the library, BMATTN_NOALLOC_MAX_WORKSPACE bytes per GPU, held from the
+ * library's first use on that GPU until the process ends; the call itself
+ * allocates and frees nothing.  args->workspace must be NULL.  A decode
+ * whose workspace (bmattn_forward_workspace_size) exceeds the static size
+ * returns BMATTN_EWORKSPACE before anything is launched.  The prefill path
+ * needs no workspace and is unchanged.
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other threads) race on it and must be
+ * serialised by the caller.  Nothing in it needs to start at zero (each
+ * value the merge reads is written earlier in the same call).  The stream
+ * must belong to the calling thread's current device. */
+#define BMATTN_NOALLOC_MAX_WORKSPACE ((size_t)96 << 20)
+int bmattn_forward_noalloc(const bmattn_fwd_args* args, const bmattn_mask_desc* desc,
+                           const bmattn_block_mask* tiles, void* stream);
 
 /* ---- column lists (kv-tile major) -------------------------------------------
  * The classes of a block mask read by kv-tile column: for column

@@ -360,3 +360,31 @@ def test_binding_rejects_wrong_id_lengths():
                            seg_q=[0] * 40, seg_k=[0] * 39)
     with pytest.raises(bm.BmattnError):
         bm._check_desc(d, "forward", torch.device("cpu"))
+
+
+def test_noalloc_forward_rejected_before_any_device_call():
+    # The entry point without allocation refuses a workspace argument and a
+    # decode whose split workspace exceeds its static scratch; neither check
+    # touches a device.
+    L = bm.lib()
+    d = _desc(mq=1, tq=2)
+    t = _tiles(d, block_m=1, block_n=64)
+    a = _args(workspace=FAKE, workspace_bytes=1 << 20)
+    assert L.bmattn_forward_noalloc(ctypes.byref(a), ctypes.byref(d), ctypes.byref(t), None) == 1
+    assert b"workspace = NULL" in L.bmattn_last_error()
+    # 2000 rows x 64 splits x 32 heads x (128 + 2) floats = 2.1 GB > 96 MiB
+    d = _desc(n=2000, mq=1, mk=32768, tq=2000, tk=2000 * 32768)
+    t = _tiles(d, block_m=1, block_n=64)
+    a = _args(num_heads=32)
+    assert L.bmattn_forward_noalloc(ctypes.byref(a), ctypes.byref(d), ctypes.byref(t), None) == 5
+    assert b"static scratch" in L.bmattn_last_error()
+    n = ctypes.c_size_t()
+    assert L.bmattn_forward_workspace_size(ctypes.byref(a), ctypes.byref(d), ctypes.byref(t),
+                                           ctypes.byref(n)) == 0
+    assert n.value > bm.NOALLOC_MAX_WORKSPACE
+
+
+def test_noalloc_limit_matches_the_header():
+    src = open(os.path.join(ROOT, "include", "bmattn.h")).read()
+    m = re.search(r"#define BMATTN_NOALLOC_MAX_WORKSPACE \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == bm.NOALLOC_MAX_WORKSPACE
