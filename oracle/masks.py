@@ -27,6 +27,10 @@ Sources:
   section "Current state in this tree" (causal + document + padding in one
   mask): the AND of the chosen terms.  The document term keeps pairs of one
   document; a negative document id marks padding, which no query sees.
+  Reading: the pieces compose by AND inside a group and by OR across groups
+  (an OR of ANDs), so that e.g. a prefix-LM mask is "causal" OR "both in the
+  prefix document".  ``terms`` is either one group (a tuple of term names)
+  or a tuple of such groups.
 """
 
 from __future__ import annotations
@@ -77,8 +81,30 @@ def visible(kind: str, Lq: int, Lk: int, *, seg_q=None, seg_k=None, role_q=None,
     raise ValueError(f"unknown mask kind {kind!r}")
 
 
-def _composed(Lq, Lk, terms, causal, *, seg_q, seg_k, role_k, turn_q, turn_k, doc_q, doc_k,
-              think_role):
+def term_groups(terms) -> tuple:
+    """The AND-groups of a composed mask: one group (a tuple of term names)
+    becomes a 1-tuple of groups; a tuple of groups is kept.  Every group is
+    non-empty and names only TERMS."""
+    terms = tuple(terms)
+    if not terms:
+        raise ValueError("a composed mask needs at least one term")
+    groups = (terms,) if all(isinstance(t, str) for t in terms) else tuple(tuple(g) for g in terms)
+    for g in groups:
+        if not g or not all(isinstance(t, str) for t in g):
+            raise ValueError(f"malformed term group {g!r}")
+    return groups
+
+
+def _composed(Lq, Lk, terms, causal, **ids):
+    """OR over the AND-groups of ``terms`` (see term_groups)."""
+    vis = np.zeros((Lq, Lk), dtype=bool)
+    for group in term_groups(terms):
+        vis |= _and_group(Lq, Lk, group, causal, **ids)
+    return vis
+
+
+def _and_group(Lq, Lk, terms, causal, *, seg_q, seg_k, role_k, turn_q, turn_k, doc_q, doc_k,
+               think_role):
     """AND of the chosen terms (any subset of TERMS, in any order)."""
     unknown = set(terms) - set(TERMS)
     if unknown:

@@ -355,6 +355,56 @@ def test_composed_document_term_equals_separate_sequences():
         assert np.array_equal(got, expect), terms
 
 
+def test_composed_or_prefix_lm_hand_worked():
+    g = _golden.load("composed_prefix_lm_7x7.txt")
+    vis = _composed((("causal",), ("document",)), 7, doc=g["doc"])
+    assert np.array_equal(vis, g["visible"].astype(bool))
+
+
+def test_composed_or_groups_hand_worked():
+    g = _golden.load("composed_or_groups_8x8.txt")
+    groups = (("causal", "strip_thinking"), ("document", "shared_prefix"))
+    ids = dict(role=g["role"], turn=g["turn"], seg=g["seg"], doc=g["doc"])
+    vis = _composed(groups, 8, **ids)
+    assert np.array_equal(vis, g["visible"].astype(bool))
+    # neither the order of the groups nor the order inside a group matters
+    assert np.array_equal(_composed((("shared_prefix", "document"), ("strip_thinking", "causal")), 8,
+                                    **ids), vis)
+
+
+def test_composed_or_prefix_lm_closed_form():
+    # causal OR (both inside the prefix document) is the lower triangle with
+    # the prefix square filled in, for any prefix length (0 .. T).
+    for T in (1, 5, 33):
+        for P in sorted({0, 1, T // 2, T}):
+            doc = np.where(np.arange(T) < P, 0, -1)
+            expect = np.tril(np.ones((T, T), bool))
+            expect[:P, :P] = True
+            assert np.array_equal(_composed((("causal",), ("document",)), T, doc=doc), expect), (T, P)
+
+
+def test_composed_one_group_is_the_and_and_groups_are_idempotent():
+    rng = np.random.default_rng(21)
+    for _ in range(6):
+        T = int(rng.integers(1, 30))
+        ids = dict(seg=np.sort(rng.integers(0, 3, T)), role=rng.integers(0, 3, T),
+                   turn=np.sort(rng.integers(0, 4, T)), doc=np.sort(rng.integers(-1, 3, T)))
+        a = tuple(t for t in masks.TERMS if rng.random() < 0.5) or ("causal",)
+        b = tuple(t for t in masks.TERMS if rng.random() < 0.5) or ("document",)
+        va = _composed(a, T, **ids)
+        assert np.array_equal(_composed((a,), T, **ids), va)
+        assert np.array_equal(_composed((a, a), T, **ids), va)
+        vab = _composed((a, b), T, **ids)
+        assert np.array_equal(_composed((b, a), T, **ids), vab)
+        assert (vab >= va).all() and (vab >= _composed(b, T, **ids)).all()
+
+
+def test_composed_rejects_malformed_groups():
+    for bad in ((), ((),), (("causal",), ()), (("causal",), "document"), (("sliding",),)):
+        with pytest.raises(ValueError):
+            _composed(bad, 3, doc=np.zeros(3))
+
+
 def test_composed_rejects_unknown_terms():
     with pytest.raises(ValueError):
         _composed(("causal", "sliding_window"), 3)

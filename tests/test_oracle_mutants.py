@@ -298,3 +298,30 @@ def test_mutant_composed_or_instead_of_and(monkeypatch):
     monkeypatch.setattr(masks, "_composed", wrong)
     assert _fails(tm.test_composed_document_strip_thinking_hand_worked,
                   tm.test_shared_prefix_groups_hand_worked) >= 1
+
+
+def test_mutant_composed_groups_anded(monkeypatch):
+    def wrong(Lq, Lk, terms, causal, **kw):  # groups combined by AND instead of OR
+        vis = np.ones((Lq, Lk), bool)
+        for group in masks.term_groups(terms):
+            vis &= masks._and_group(Lq, Lk, group, causal, **kw)
+        return vis
+
+    monkeypatch.setattr(masks, "_composed", wrong)
+    assert _fails(tm.test_composed_or_prefix_lm_hand_worked, tm.test_composed_or_groups_hand_worked,
+                  tm.test_composed_or_prefix_lm_closed_form) == 3
+
+
+def test_mutant_composed_or_and_swapped(monkeypatch):
+    def wrong(Lq, Lk, terms, causal, **kw):  # OR inside each group, AND across groups
+        vis = np.ones((Lq, Lk), bool)
+        for group in masks.term_groups(terms):
+            any_term = np.zeros((Lq, Lk), bool)
+            for t in group:
+                any_term |= masks._and_group(Lq, Lk, (t,), causal, **kw)
+            vis &= any_term
+        return vis
+
+    monkeypatch.setattr(masks, "_composed", wrong)
+    assert _fails(tm.test_composed_or_prefix_lm_hand_worked, tm.test_composed_or_groups_hand_worked,
+                  tm.test_composed_or_prefix_lm_closed_form) >= 2
