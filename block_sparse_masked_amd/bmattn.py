@@ -24,6 +24,24 @@ MASK_FULL, MASK_CAUSAL, MASK_SHARED_PREFIX, MASK_STRIP_THINKING, MASK_COMPOSED =
 KIND_CODES = {"full": MASK_FULL, "causal": MASK_CAUSAL, "shared_prefix": MASK_SHARED_PREFIX,
               "strip_thinking": MASK_STRIP_THINKING, "composed": MASK_COMPOSED}
 TERM_CODES = {"causal": 1, "document": 2, "shared_prefix": 4, "strip_thinking": 8}
+MAX_TERM_GROUPS = 4
+
+
+def term_bits(terms) -> int:
+    """The C ABI's terms word of a COMPOSED mask: an int passes through; one
+    group (term names) is its OR of TERM_CODES; a sequence of groups puts
+    group g in bits 4g .. 4g+3 (an OR of AND-groups)."""
+    if isinstance(terms, int):
+        return terms
+    terms = tuple(terms)
+    groups = (terms,) if all(isinstance(t, str) for t in terms) else terms
+    _require(0 < len(groups) <= MAX_TERM_GROUPS, "terms",
+             f"a composed mask takes 1 to {MAX_TERM_GROUPS} term groups (got {len(groups)})")
+    bits = 0
+    for g, group in enumerate(groups):
+        _require(not isinstance(group, str) and len(group) > 0, "terms", f"malformed term group {group!r}")
+        bits |= sum(TERM_CODES[t] for t in set(group)) << (4 * g)
+    return bits
 F32, BF16 = 0, 1
 TILE_EMPTY, TILE_PARTIAL, TILE_FULL = 0, 1, 2
 STATUS = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "EALIGN", 4: "EHIP", 5: "EWORKSPACE"}
@@ -188,7 +206,7 @@ class MaskDesc:
     # For a description relabelled from duplicated answers: (the description
     # with the layout's own ids, role_q, loss_role, history_role).
     duplicated_from: Optional[tuple] = None
-    terms: int = 0  # COMPOSED: OR of TERM_CODES
+    terms: int = 0  # COMPOSED: term groups, group g in bits 4g..4g+3 (see term_bits)
     doc_q: Optional[torch.Tensor] = None
     doc_k: Optional[torch.Tensor] = None
 
@@ -201,8 +219,9 @@ class MaskDesc:
         layout with duplicated answer spans (role_q, role_k with loss_role
         and history_role, turn_q, turn_k) and returns the STRIP_THINKING
         description that bmattn_duplicated_answer_ids relabels them to; kind
-        "composed" takes ``terms`` (names of TERM_CODES, or their OR) and the
-        ids those terms read (document: doc_q, doc_k)."""
+        "composed" takes ``terms`` (one group of TERM_CODES names, a sequence
+        of such groups -- an OR of ANDs --, or the packed int; see term_bits)
+        and the ids those terms read (document: doc_q, doc_k)."""
         if kind == "strip_thinking_duplicated":
             src = MaskDesc.create("strip_thinking", cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                                   max_seqlen_k, device=device, role_k=role_k, turn_q=turn_q,
@@ -216,7 +235,7 @@ class MaskDesc:
         tq = int(cq[-1].item()) if n >= 0 else 0
         tk = int(ck[-1].item()) if n >= 0 else 0
         if kind == MASK_COMPOSED:
-            bits = terms if isinstance(terms, int) else sum(TERM_CODES[t] for t in set(terms))
+            bits = term_bits(terms)
         else:
             bits = 0
         return MaskDesc(kind, n, int(max_seqlen_q), int(max_seqlen_k), tq, tk, cq, ck,

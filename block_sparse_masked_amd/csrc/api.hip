@@ -39,6 +39,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Decode splits: consecutive entries of a row's kv-tile list per workgroup.
 constexpr int32_t kDecodeSplitTiles = 8;
 
+// The union of a COMPOSED description's term groups (4-bit nibbles).
+int32_t term_union(int32_t groups) {
+  return (groups | (groups >> 4) | (groups >> 8) | (groups >> 12)) & 15;
+}
+
 int check_desc(const bmattn_mask_desc* d) {
   if (d == nullptr) return fail(BMATTN_EINVAL, "mask description is NULL");
   if (d->kind < BMATTN_MASK_FULL || d->kind > BMATTN_MASK_COMPOSED)
@@ -58,14 +63,17 @@ int check_desc(const bmattn_mask_desc* d) {
       (d->role_k == nullptr || d->turn_q == nullptr || d->turn_k == nullptr))
     return fail(BMATTN_EINVAL, "STRIP_THINKING needs role_k, turn_q and turn_k");
   if (d->kind == BMATTN_MASK_COMPOSED) {
-    if (d->terms <= 0 || d->terms > 15)
-      return fail(BMATTN_EINVAL, "COMPOSED needs terms, a non-empty OR of BMATTN_TERM_* (got %d)",
+    if (d->terms <= 0 || d->terms > 0xffff)
+      return fail(BMATTN_EINVAL,
+                  "COMPOSED needs terms: up to four groups of BMATTN_TERM_* bits, group g in bits "
+                  "4g..4g+3, at least one non-empty (got %d)",
                   d->terms);
-    if ((d->terms & BMATTN_TERM_DOCUMENT) && (d->doc_q == nullptr || d->doc_k == nullptr))
+    const int32_t any = term_union(d->terms);
+    if ((any & BMATTN_TERM_DOCUMENT) && (d->doc_q == nullptr || d->doc_k == nullptr))
       return fail(BMATTN_EINVAL, "the DOCUMENT term needs doc_q and doc_k");
-    if ((d->terms & BMATTN_TERM_SHARED_PREFIX) && (d->seg_q == nullptr || d->seg_k == nullptr))
+    if ((any & BMATTN_TERM_SHARED_PREFIX) && (d->seg_q == nullptr || d->seg_k == nullptr))
       return fail(BMATTN_EINVAL, "the SHARED_PREFIX term needs seg_q and seg_k");
-    if ((d->terms & BMATTN_TERM_STRIP_THINKING) &&
+    if ((any & BMATTN_TERM_STRIP_THINKING) &&
         (d->role_k == nullptr || d->turn_q == nullptr || d->turn_k == nullptr))
       return fail(BMATTN_EINVAL, "the STRIP_THINKING term needs role_k, turn_q and turn_k");
   } else if (d->terms != 0) {
@@ -80,11 +88,17 @@ MaskDev to_dev(const bmattn_mask_desc* d) {
   m.n_seqs = d->n_seqs;
   m.think_role = d->think_role;
   switch (d->kind) {
-    case BMATTN_MASK_FULL: m.terms = 0; break;
-    case BMATTN_MASK_CAUSAL: m.terms = BMATTN_TERM_CAUSAL; break;
-    case BMATTN_MASK_SHARED_PREFIX: m.terms = BMATTN_TERM_CAUSAL | BMATTN_TERM_SHARED_PREFIX; break;
-    case BMATTN_MASK_STRIP_THINKING: m.terms = BMATTN_TERM_CAUSAL | BMATTN_TERM_STRIP_THINKING; break;
-    default: m.terms = d->terms; break;
+    case BMATTN_MASK_FULL: m.groups = 0; break;
+    case BMATTN_MASK_CAUSAL: m.groups = BMATTN_TERM_CAUSAL; break;
+    case BMATTN_MASK_SHARED_PREFIX: m.groups = BMATTN_TERM_CAUSAL | BMATTN_TERM_SHARED_PREFIX; break;
+    case BMATTN_MASK_STRIP_THINKING: m.groups = BMATTN_TERM_CAUSAL | BMATTN_TERM_STRIP_THINKING; break;
+    default: m.groups = d->terms; break;
+  }
+  m.terms = term_union(m.groups);
+  m.causal_all = m.groups != 0;
+  for (int g = 0; g < 4; ++g) {
+    const int32_t t = (m.groups >> (4 * g)) & 15;
+    if (t != 0 && !(t & BMATTN_TERM_CAUSAL)) m.causal_all = 0;
   }
   m.total_q = d->total_q;
   m.total_k = d->total_k;

@@ -224,15 +224,14 @@ __device__ __forceinline__ void store_rows(void* dst, int64_t off_elems, const f
   }
 }
 
-// The element predicate through the mask's terms (every kind is a set of
-// terms: m.terms), wave-uniform: query row i with ids q, key j with
-// segment, role, turn and document ids.  Same condition as visible_k().
+// The element predicate through the mask's term groups (every kind is an
+// OR of AND-groups: m.groups), wave-uniform: query row i with ids q, key j
+// with segment, role, turn and document ids.  Same condition as visible_k().
 __device__ __forceinline__ bool visible_rt(const MaskDev& m, const SeqBounds& b, int i, QIds q,
                                            int j, int32_t kseg, int32_t krole, int32_t kturn,
                                            int32_t kdoc) {
   const bool in = (i < b.lq) & (j < b.lk);
-  const bool causal = !(m.terms & BMATTN_TERM_CAUSAL) | (j <= b.lk - b.lq + i);
-  return in & causal & composed_ids_ok(m.terms, m.think_role, q, kseg, krole, kturn, kdoc);
+  return in & composed_ok(m.groups, m.think_role, j <= b.lk - b.lq + i, q, kseg, krole, kturn, kdoc);
 }
 
 // Key ids in term order (segment, role, turn, document) from load_kids().

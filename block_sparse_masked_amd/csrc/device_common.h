@@ -13,14 +13,20 @@
 namespace bmattn {
 
 // Mask description as the kernels see it (kernel-argument friendly copy).
-// `terms` holds the kind's predicate as BMATTN_TERM_* bits for every kind
-// (FULL: none; CAUSAL: causal; SHARED_PREFIX / STRIP_THINKING: causal and
-// the id term; COMPOSED: the description's terms), set by the host.
+// Every kind is an OR of AND-groups of BMATTN_TERM_* bits, set by the host:
+// `groups` holds up to four groups, group g in bits 4g .. 4g+3 (FULL: 0,
+// which means every pair; CAUSAL: {causal}; SHARED_PREFIX / STRIP_THINKING:
+// {causal, the id term}; COMPOSED: the description's terms).  `terms` is the
+// union of the groups (which id arrays are read) and `causal_all` tells
+// whether every group holds the causal term (then no pair above the
+// diagonal is visible).
 struct MaskDev {
   int32_t kind;
   int32_t n_seqs;
   int32_t think_role;
   int32_t terms;
+  int32_t groups;
+  int32_t causal_all;
   int64_t total_q, total_k;
   const int32_t* cu_q;
   const int32_t* cu_k;
@@ -113,6 +119,21 @@ __device__ __forceinline__ bool composed_ids_ok(int32_t terms, int32_t think_rol
   return doc & pre & strip;
 }
 
+// One pair through an OR of AND-groups: visible when some non-empty group
+// passes, its causal term on `causal_ok` (j <= p(i)) and its id terms on the
+// ids.  groups == 0 (FULL) passes every pair.
+__device__ __forceinline__ bool composed_ok(int32_t groups, int32_t think_role, bool causal_ok, QIds q,
+                                            int32_t kseg, int32_t krole, int32_t kturn, int32_t kdoc) {
+  if (groups == 0) return true;
+  bool v = false;
+  for (int32_t gs = groups; gs != 0; gs >>= 4) {  // wave-uniform: one pass per group
+    const int32_t t = gs & 15;
+    v |= (t != 0) & (!(t & BMATTN_TERM_CAUSAL) | causal_ok) &
+         composed_ids_ok(t, think_role, q, kseg, krole, kturn, kdoc);
+  }
+  return v;
+}
+
 // Element predicate: is key j of the sequence visible to its query row i?
 // Query row i sits at position lk - lq + i; the causal condition keeps the
 // diagonal (j <= position).  Pairs outside the sequence are not visible.
@@ -128,8 +149,7 @@ __device__ __forceinline__ bool visible_k(const MaskDev& m, const SeqBounds& b, 
   if constexpr (KIND == BMATTN_MASK_STRIP_THINKING)
     return causal & !((kid.a == m.think_role) & (kid.b < qi.turn));
   // COMPOSED
-  const bool c = !(m.terms & BMATTN_TERM_CAUSAL) | (j <= b.lk - b.lq + i);
-  return in & c & composed_ids_ok(m.terms, m.think_role, qi, kid.a, kid.b, kid.c, kid.d);
+  return in & composed_ok(m.groups, m.think_role, j <= b.lk - b.lq + i, qi, kid.a, kid.b, kid.c, kid.d);
 }
 
 __device__ __forceinline__ bool visible_ids(const MaskDev& m, const SeqBounds& b, int i, QIds qi,

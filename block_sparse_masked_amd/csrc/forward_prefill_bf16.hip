@@ -318,17 +318,22 @@ __device__ __forceinline__ void s_product(const char* Ks, const bf16x8 (&q)[D / 
 //    lk - lq + qi) (FULL: lk - 1).  Key offsets grow with the bit index, so
 //    the visible bits are a prefix whose length follows from lim directly;
 //  * shared-prefix and strip-thinking then AND in the key-id condition, the
-//    ids read from the tile's id stage 8 keys at a time.
+//    ids read from the tile's id stage 8 keys at a time;
+//  * COMPOSED: each term group ANDs its id terms with its own limit (causal
+//    or bounds only), and the groups are ORed.
+// The prefix of the bits whose keys lie at or before key lim.
+__device__ __forceinline__ uint32_t prefix_bits(int lim, int kt, int g) {
+  const int n = lim - kt * kBN - 8 * g + 1;  // keys 16 c + e < n
+  const int count = n <= 0 ? 0 : min(32, 8 * (n >> 4) + min(n & 15, 8));
+  return count >= 32 ? 0xffffffffu : ((1u << count) - 1u);
+}
 template <int D, int KIND>
 __device__ __forceinline__ uint32_t visible_bits(const char* kstage, const FwdDev& p,
                                                  const SeqBounds& sb, int kt, int qi, QIds qids,
                                                  int g) {
-  const bool causal = (KIND == BMATTN_MASK_COMPOSED) ? (p.mask.terms & BMATTN_TERM_CAUSAL) != 0
-                                                    : KIND != BMATTN_MASK_FULL;
+  const bool causal = KIND != BMATTN_MASK_FULL && KIND != BMATTN_MASK_COMPOSED;
   const int lim = causal ? min(sb.lk - 1, sb.lk - sb.lq + qi) : sb.lk - 1;
-  const int n = lim - kt * kBN - 8 * g + 1;  // keys 16 c + e < n are visible
-  const int count = n <= 0 ? 0 : min(32, 8 * (n >> 4) + min(n & 15, 8));
-  uint32_t bits = qi < sb.lq ? (count >= 32 ? 0xffffffffu : ((1u << count) - 1u)) : 0u;
+  uint32_t bits = qi < sb.lq ? prefix_bits(lim, kt, g) : 0u;
   if constexpr (KIND == BMATTN_MASK_SHARED_PREFIX || KIND == BMATTN_MASK_STRIP_THINKING) {
     const int32_t* ida = reinterpret_cast<const int32_t*>(kstage + Lay<D>::kIds);
     const int32_t* idb = ida + kBN;
@@ -356,8 +361,10 @@ __device__ __forceinline__ uint32_t visible_bits(const char* kstage, const FwdDe
   if constexpr (KIND == BMATTN_MASK_COMPOSED) {
     // The four staged arrays: segment, role, turn, document (an array the
     // terms do not read holds stale values that composed_ids_ok ignores).
+    // `bits` holds the in-bounds keys; the causal prefix is cb.
+    const uint32_t cb = qi < sb.lq ? prefix_bits(min(sb.lk - 1, sb.lk - sb.lq + qi), kt, g) : 0u;
     const int32_t* ida = reinterpret_cast<const int32_t*>(kstage + Lay<D>::kIds);
-    uint32_t keep = 0;
+    uint32_t vis = 0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int j0 = 16 * c + 8 * g;
@@ -369,12 +376,18 @@ __device__ __forceinline__ uint32_t visible_bits(const char* kstage, const FwdDe
         v[a][0] = x0.x; v[a][1] = x0.y; v[a][2] = x0.z; v[a][3] = x0.w;
         v[a][4] = x1.x; v[a][5] = x1.y; v[a][6] = x1.z; v[a][7] = x1.w;
       }
+      for (int32_t gs = p.mask.groups; gs != 0; gs >>= 4) {  // wave-uniform
+        const int32_t t = gs & 15;
+        if (t == 0) continue;
+        uint32_t keep = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        keep |= (uint32_t)composed_ids_ok(p.mask.terms, p.mask.think_role, qids, v[0][e], v[1][e],
-                                          v[2][e], v[3][e]) << (8 * c + e);
+        for (int e = 0; e < 8; ++e)
+          keep |= (uint32_t)composed_ids_ok(t, p.mask.think_role, qids, v[0][e], v[1][e], v[2][e], v[3][e])
+                  << (8 * c + e);
+        vis |= keep & ((t & BMATTN_TERM_CAUSAL) ? cb : bits);
+      }
     }
-    bits &= keep;
+    bits = vis;
   }
   return bits;
 }

@@ -123,8 +123,9 @@ __device__ uint8_t classify_tile(const MaskDev& m, const SeqBounds& b, int qlo, 
   return any_hid ? BMATTN_TILE_PARTIAL : BMATTN_TILE_FULL;
 }
 
-// COMPOSED masks.  The queries of a row tile fall into a few groups of
-// equal ids (segment, turn, document); the kernel lists them (up to
+// COMPOSED masks of one term group (an AND).  The queries of a row tile
+// fall into a few groups of equal ids (segment, turn, document); the
+// kernel lists them (up to
 // kMaxGroups, with the largest row of each) before classifying.  With the
 // causal term, pair (i, j) is visible iff j <= i + off and the key's ids
 // pass the group's id terms, so a tile is
@@ -150,7 +151,7 @@ __device__ uint8_t classify_tile_groups(const MaskDev& m, const SeqBounds& b, in
   const int qhi = min(qlo + BM, b.lq);
   const int khi = min(klo + BN, b.lk);
   const bool inside = (qlo + BM <= b.lq) && (klo + BN <= b.lk);
-  const bool causal = (m.terms & BMATTN_TERM_CAUSAL) != 0;
+  const bool causal = m.causal_all != 0;
   const int64_t off = (int64_t)b.lk - b.lq;
   if (causal && (int64_t)klo > (int64_t)(qhi - 1) + off) return BMATTN_TILE_EMPTY;
   const bool causal_full = !causal || ((int64_t)klo + BN - 1 <= (int64_t)qlo + off);
@@ -181,7 +182,7 @@ __device__ uint8_t classify_tile_summary(const MaskDev& m, const SeqBounds& b, i
   if (qlo >= b.lq || klo >= b.lk) return BMATTN_TILE_EMPTY;
   const int qhi = min(qlo + BM, b.lq);
   const int khi = min(klo + BN, b.lk);
-  const bool causal = (m.terms & BMATTN_TERM_CAUSAL) != 0;
+  const bool causal = m.causal_all != 0;
   const int64_t off = (int64_t)b.lk - b.lq;
   if (causal && (int64_t)klo > (int64_t)(qhi - 1) + off) return BMATTN_TILE_EMPTY;
   if ((!causal || (int64_t)hmin + off >= (int64_t)khi - 1) && tcnt == khi - klo) {
@@ -201,17 +202,20 @@ __device__ uint8_t classify_tile_enum(const MaskDev& m, const SeqBounds& b, int 
   const int qhi = min(qlo + BM, b.lq);
   const int khi = min(klo + BN, b.lk);
   const bool inside = (qlo + BM <= b.lq) && (klo + BN <= b.lk);
-  const bool causal = (m.terms & BMATTN_TERM_CAUSAL) != 0;
   const int64_t off = (int64_t)b.lk - b.lq;
-  if (causal && (int64_t)klo > (int64_t)(qhi - 1) + off) return BMATTN_TILE_EMPTY;
+  if (m.causal_all && (int64_t)klo > (int64_t)(qhi - 1) + off) return BMATTN_TILE_EMPTY;
+  // A group that is the causal term alone shows every pair on or below the
+  // diagonal: a tile inside the sequence and wholly below it is FULL.
+  bool causal_alone = false;
+  for (int32_t gs = m.groups; gs != 0; gs >>= 4) causal_alone |= (gs & 15) == BMATTN_TERM_CAUSAL;
+  if (causal_alone && inside && (int64_t)klo + BN - 1 <= (int64_t)qlo + off) return BMATTN_TILE_FULL;
   bool any_vis = false, any_hid = !inside;
   for (int j = klo; j < khi; ++j) {
     const int u = j - k0;
     const int32_t a0 = kid[u], a1 = kid[kw + u], a2 = kid[2 * kw + u], a3 = kid[3 * kw + u];
     for (int i = qlo; i < qhi; ++i) {
       const QIds q{qs[i - qlo], qt[i - qlo], qd[i - qlo]};
-      const bool v = (!causal || (int64_t)j <= off + i) &&
-                     composed_ids_ok(m.terms, m.think_role, q, a0, a1, a2, a3);
+      const bool v = composed_ok(m.groups, m.think_role, (int64_t)j <= off + i, q, a0, a1, a2, a3);
       any_vis |= v;
       any_hid |= !v;
       if (any_vis && any_hid) return BMATTN_TILE_PARTIAL;
@@ -315,7 +319,8 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev 
       const int g = l < 0 ? -1 - l : -1 - lead[l];
       if (g < kMaxGroups) atomicMax(&rg.hi[g], qlo + i);
     }
-    if (tid == 0) rg.n = nlead <= kMaxGroups ? nlead : -1;
+    // (an OR of several term groups always enumerates)
+    if (tid == 0) rg.n = (nlead <= kMaxGroups && (m.groups >> 4) == 0) ? nlead : -1;
     __syncthreads();
   }
 
@@ -344,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev 
   // visible: those tiles classify as EMPTY without reading ids, so their
   // ids are not staged.
   int64_t kvis = b.lk;
-  if ((m.terms & BMATTN_TERM_CAUSAL) && qlo < b.lq)
+  if (m.causal_all && qlo < b.lq)
     kvis = std::min<int64_t>(b.lk, (int64_t)std::min(qlo + BM, b.lq) + ((int64_t)b.lk - b.lq));
   for (int c0 = 0; c0 < t.n_kt; c0 += tpc) {
     const int bidx = c0 + tid;

@@ -71,7 +71,11 @@ typedef enum {
  *   STRIP_THINKING  j <= p(i) and not (role_k[j] == think_role and
  *                                       turn_k[j] < turn_q[i])
  *                                                           [XORL "Mask specifications"]
- *   COMPOSED        the AND of the terms set in desc->terms:
+ *   COMPOSED        an OR of up to four AND-groups of terms: desc->terms
+ *                   holds group g in bits 4g .. 4g+3 (BMATTN_TERM_GROUP),
+ *                   and key j is visible when it passes every term of at
+ *                   least one non-empty group.  One group (terms <= 15) is
+ *                   the plain AND.  The terms:
  *     BMATTN_TERM_CAUSAL          j <= p(i)
  *     BMATTN_TERM_DOCUMENT        doc_k[j] == doc_q[i] and doc_k[j] >= 0
  *                                 (a negative document id marks padding)
@@ -82,6 +86,10 @@ typedef enum {
  *                                  document, shared-prefix and strip-thinking
  *                                  pieces; "Current state in this tree":
  *                                  causal + document + padding in one mask]
+ *                                 [reading: AND inside a group, OR across
+ *                                  groups, e.g. a prefix-LM mask is
+ *                                  {CAUSAL} OR {DOCUMENT} with the prefix
+ *                                  in document 0 and the rest in -1]
  *   (CAUSAL is COMPOSED with {CAUSAL}, SHARED_PREFIX with {CAUSAL,
  *   SHARED_PREFIX}, STRIP_THINKING with {CAUSAL, STRIP_THINKING}.)
  * Packed documents are sequences of cu_seqlens with the CAUSAL kind: every
@@ -96,13 +104,15 @@ typedef enum {
   BMATTN_MASK_COMPOSED = 4
 } bmattn_mask_kind;
 
-/* Terms of a COMPOSED mask (bit set in bmattn_mask_desc.terms). */
+/* Terms of a COMPOSED mask (bits of one group in bmattn_mask_desc.terms). */
 enum {
   BMATTN_TERM_CAUSAL = 1,
   BMATTN_TERM_DOCUMENT = 2,
   BMATTN_TERM_SHARED_PREFIX = 4,
   BMATTN_TERM_STRIP_THINKING = 8
 };
+/* Group g (0 .. 3) of a COMPOSED mask's terms word: the groups are ORed. */
+#define BMATTN_TERM_GROUP(g, bits) ((int32_t)(bits) << (4 * (g)))
 
 typedef enum { BMATTN_F32 = 0, BMATTN_BF16 = 1 } bmattn_dtype;
 
@@ -119,7 +129,7 @@ enum { BMATTN_TILE_EMPTY = 0, BMATTN_TILE_PARTIAL = 1, BMATTN_TILE_FULL = 2 };
  * Id arrays are indexed by packed query row (…_q) or packed key row (…_k);
  * for self-attention pass the same array for both sides.  Only the ids the
  * kind reads must be non-NULL (SHARED_PREFIX: seg_q, seg_k; STRIP_THINKING:
- * role_k, turn_q, turn_k; COMPOSED: those of its terms, DOCUMENT: doc_q,
+ * role_k, turn_q, turn_k; COMPOSED: those of any group's terms, DOCUMENT: doc_q,
  * doc_k).
  */
 typedef struct {
@@ -130,7 +140,7 @@ typedef struct {
   int64_t total_q;        /* cu_seqlens_q[n_seqs]: rows of Q, O, ids_q         */
   int64_t total_k;        /* cu_seqlens_k[n_seqs]: rows of K, V, ids_k         */
   int32_t think_role;     /* role value of think tokens (STRIP_THINKING)       */
-  int32_t terms;          /* COMPOSED: OR of BMATTN_TERM_* (non-zero); else 0  */
+  int32_t terms;          /* COMPOSED: term groups (1..0xffff, see above); else 0 */
   const int32_t* cu_seqlens_q; /* [n_seqs + 1], non-decreasing, starts at 0   */
   const int32_t* cu_seqlens_k; /* [n_seqs + 1], non-decreasing, starts at 0   */
   const int32_t* seg_q;   /* [total_q] segment id of each query (0 = prefix)   */

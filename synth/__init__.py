@@ -21,6 +21,7 @@ from .workloads import (  # noqa: F401
     strip_thinking,
     strip_thinking_duplicated,
     shared_prefix_groups,
+    prefix_lm,
     paged_decode,
     config,
     CONFIG_NAMES,

@@ -63,7 +63,7 @@ class Layout:
     turn_k: Optional[np.ndarray] = None
     doc_q: Optional[np.ndarray] = None
     doc_k: Optional[np.ndarray] = None
-    terms: tuple = ()  # composed kind: the ANDed terms
+    terms: tuple = ()  # composed kind: one group of ANDed terms, or a tuple of groups (ORed)
     think_role: int = THINK_ROLE
     loss_role: int = LOSS_ROLE
     history_role: int = HISTORY_ROLE
@@ -222,6 +222,18 @@ def shared_prefix_groups(n_groups: int = 4, prefix: int = 1024, n_suffix: int = 
                          "suffix": suffix, "pad": pad})
 
 
+def prefix_lm(prefixes=(1024,), lengths=(4096,), H: int = 8, D: int = 128,
+              dtype: str = "bf16") -> Layout:
+    """Prefix-LM sequences: the first prefixes[s] tokens of sequence s see
+    each other both ways, the rest is causal -- the composed mask (causal)
+    OR (document), with the prefix in document 0 and the rest in -1."""
+    lens = [int(n) for n in lengths]
+    doc = np.concatenate([np.where(np.arange(n) < p, 0, -1) for p, n in zip(prefixes, lens)]
+                         ).astype(np.int32) if lens else np.zeros(0, np.int32)
+    return Layout("prefix_lm", "composed", dtype, H, D, lens, lens, doc_q=doc, doc_k=doc,
+                  terms=(("causal",), ("document",)))
+
+
 def paged_decode(seed: int = 0, n_seqs: int = 64, lo: int = 512, hi: int = 32768,
                  page_size: int = 16, H: int = 32, D: int = 128, dtype: str = "bf16") -> Layout:
     """One new query per sequence over a paged context of ragged length."""
@@ -329,8 +341,15 @@ def random_layout(rng: np.random.Generator, kind: str, n_seqs: int = 3, max_len:
         # a random non-empty subset of the terms, with every id array drawn:
         # documents as runs (some padding, id -1), segments as runs with 0
         # first inside each document, roles and turns as in strip_thinking
-        while not terms:
-            terms = tuple(t for t in TERMS if rng.random() < 0.6)
+        # one AND-group, or (half the time) an OR of two or three groups
+        n_groups = 1 if rng.random() < 0.5 else int(rng.integers(2, 4))
+        groups = []
+        for _ in range(n_groups):
+            g = ()
+            while not g:
+                g = tuple(t for t in TERMS if rng.random() < 0.6)
+            groups.append(g)
+        terms = groups[0] if n_groups == 1 else tuple(groups)
         sp, rp, tp, dp = [], [], [], []
         for L in lens_k:
             doc = np.zeros(L, np.int32)

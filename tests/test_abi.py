@@ -182,8 +182,12 @@ def test_gather_and_debug_and_validate_rejections():
 @pytest.mark.parametrize("terms,docs,ids,ok", [
     (1, True, True, True), (15, True, True, True), (2, True, False, True),
     (0, True, True, False),    # COMPOSED needs at least one term
-    (16, True, True, False),   # unknown term bit
+    (16, True, True, True),    # group 1 alone ({causal})
+    (0x8421, True, True, True),  # four groups
+    (0x10000, True, True, False),  # beyond four groups
     (-1, True, True, False),
+    (0x21, False, True, False),    # DOCUMENT in group 1 without doc arrays
+    (0x4001, True, False, False),  # SHARED_PREFIX in group 3 without segments
     (2, False, True, False),   # DOCUMENT without doc arrays
     (4, True, False, False),   # SHARED_PREFIX without segments
     (8, True, False, False),   # STRIP_THINKING without roles / turns
@@ -191,6 +195,17 @@ def test_gather_and_debug_and_validate_rejections():
 def test_composed_description_validation(terms, docs, ids, ok):
     rc, *_ = _call_shape(_desc(kind=bm.MASK_COMPOSED, terms=terms, docs=docs, ids=ids), 128, 64)
     assert (rc == 0) == ok, bm.lib().bmattn_last_error()
+
+
+def test_term_bits_packs_groups():
+    assert bm.term_bits(("causal", "document")) == 3
+    assert bm.term_bits((("causal",), ("document",))) == 0x21
+    assert bm.term_bits((("strip_thinking",), ("document", "causal"), ("shared_prefix",),
+                         ("causal",))) == 0x1438
+    assert bm.term_bits(0x21) == 0x21
+    for bad in ((), ((),), ((("causal",),) * 5)):
+        with pytest.raises(bm.BmattnError):
+            bm.term_bits(bad)
 
 
 def test_terms_rejected_on_plain_kinds():

@@ -109,6 +109,25 @@ def test_backward_random_layouts(kind, D):
         check_grads(got, ref, f"{kind}/D{D}")
 
 
+@pytest.mark.parametrize("groups", [(("causal",), ("document",)),
+                                    (("causal", "strip_thinking"), ("document", "shared_prefix"))])
+def test_backward_composed_or_groups(groups):
+    # An OR of AND-groups: column lists bit for bit and the gradients.
+    rng = np.random.default_rng(90 + len(groups[1]))
+    lay = synth.random_layout(rng, "composed", n_seqs=3, max_len=330, min_len=1, H=2, D=128, dtype="bf16")
+    lay.terms = groups
+    say(f"backward composed OR {groups} lens={lay.seqlens_q}")
+    check_cols(lay, _hip.desc_for(lay), 64, 128)
+    (q, k, v, do), got = run_backward(lay, seed=1)
+    ref = obackward.backward(lay, q.cpu(), k.cpu(), v.cpu(), do.cpu())
+    check_grads(got, ref, f"composed OR {groups}")
+    pl = synth.prefix_lm(prefixes=(100, 0, 257), lengths=(400, 130, 257), H=2)
+    say("backward prefix-LM")
+    (q, k, v, do), got = run_backward(pl, seed=2)
+    ref = obackward.backward(pl, q.cpu(), k.cpu(), v.cpu(), do.cpu())
+    check_grads(got, ref, "prefix-LM")
+
+
 def test_backward_fewer_queries_than_keys_and_empty_sequences():
     # Queries at the end of longer contexts, empty sequences, a sequence with
     # more queries than keys (rows that see nothing get dQ = 0).

@@ -102,6 +102,37 @@ def test_decode_layouts(kind, paged, dtype, D):
         _hip.check_close(o, lse, O, L, dtype, f"decode {kind}")
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_prefix_lm_prefill_decode_and_paged(dtype, D):
+    # The OR composition (causal) OR (document): prefix-LM sequences with the
+    # prefix inside a tile, on a tile edge and the whole sequence; prefill on
+    # contiguous and paged K/V, then decode of the last 3 positions.
+    lay = synth.prefix_lm(prefixes=(77, 128, 300), lengths=(500, 640, 300), H=2, D=D, dtype=dtype)
+    say(f"prefix-LM prefill {dtype} D={D}")
+    o, lse, q, k, v, desc, t = _hip.run_dense(lay, seed=3)
+    O, L = _hip.oracle_dense(lay, q, k, v)
+    _hip.check_close(o, lse, O, L, dtype, "prefix-LM prefill")
+    pl = synth.Layout("prefix_lm", "composed", dtype, 2, D, lay.seqlens_q, lay.seqlens_k, doc_q=lay.doc_q,
+                      doc_k=lay.doc_k, terms=lay.terms, paged=True, page_size=16)
+    qp, kp, vp, bt = synth.make_paged_kv(pl, seed=4, device="cpu", extra_pages=2)
+    say(f"prefix-LM paged {dtype} D={D}")
+    op, lp = bm.forward(qp.to(DEV), kp.to(DEV), vp.to(DEV), _hip.desc_for(pl), bm.build_block_mask(
+        _hip.desc_for(pl), 128, 64), block_table=bt.to(DEV))
+    Op, Lp = oforward.forward(pl, qp, k_pool=kp, v_pool=vp, block_table=bt)
+    _hip.check_close(op, lp, Op, Lp, dtype, "prefix-LM paged")
+    # decode: the last 3 queries of each sequence against its whole context
+    cu = np.concatenate([[0], np.cumsum(lay.seqlens_k)])
+    dq = np.concatenate([lay.doc_k[cu[s + 1] - 3:cu[s + 1]] for s in range(lay.n_seqs)]).astype(np.int32)
+    dl = synth.Layout("prefix_lm_decode", "composed", dtype, 2, D, [3] * lay.n_seqs, lay.seqlens_k,
+                      doc_q=dq, doc_k=lay.doc_k, terms=lay.terms)
+    qd, kd, vd = synth.make_dense_qkv(dl, seed=5, device="cpu")
+    ddesc = _hip.desc_for(dl)
+    say(f"prefix-LM decode {dtype} D={D}")
+    od, ld = bm.forward(qd.to(DEV), kd.to(DEV), vd.to(DEV), ddesc, bm.build_block_mask(ddesc, 1, 64))
+    Od, Ld = oforward.forward(dl, qd, kd, vd)
+    _hip.check_close(od, ld, Od, Ld, dtype, "prefix-LM decode")
+
+
 def test_empty_sequences_and_rows_without_keys():
     # Sequences of length 0 write nothing; with more queries than keys the
     # first rows see no key: O = 0 and LSE = -inf.

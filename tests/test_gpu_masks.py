@@ -219,6 +219,42 @@ def test_composed_every_term_set(terms):
             _hip.check_dense(lay, desc, t)
 
 
+OR_GROUPS = [
+    (("causal",), ("document",)),  # prefix-LM
+    (("causal", "strip_thinking"), ("document", "shared_prefix")),
+    (("document",), ("shared_prefix",), ("causal",)),
+    (("causal", "shared_prefix"), ("causal", "strip_thinking")),
+    (("strip_thinking",), ("document", "causal"), ("shared_prefix", "causal"), ("causal",)),
+]
+
+
+@pytest.mark.parametrize("gi", range(len(OR_GROUPS)))
+def test_composed_or_groups(gi):
+    # OR of AND-groups on random layouts: tile classes, lists and the dense
+    # mask bit for bit against the oracle (the classifier enumerates them).
+    groups = OR_GROUPS[gi]
+    rng = np.random.default_rng(500 + gi)
+    for trial in range(2):
+        lay = synth.random_layout(rng, "composed", n_seqs=3, max_len=260)
+        lay.terms = groups
+        desc = _hip.desc_for(lay)
+        for BM, BN in ((128, 64), (64, 128), (16, 16), (1, 64)):
+            say(f"composed OR groups={groups} trial={trial} lens={lay.seqlens_k} {BM}x{BN}")
+            t = _hip.check_tiles(lay, desc, BM, BN)
+            _hip.check_dense(lay, desc, t)
+
+
+def test_prefix_lm_tiles():
+    # Prefix-LM sequences of several prefix lengths (0, inside a tile, on a
+    # tile edge, the whole sequence): tiles at the forward's and the
+    # backward's shapes and the decode shape.
+    lay = synth.prefix_lm(prefixes=(0, 77, 128, 300, 1000), lengths=(300, 900, 640, 300, 1000), H=1)
+    desc = _hip.desc_for(lay)
+    for BM, BN in ((128, 64), (64, 128), (1, 64)):
+        say(f"prefix-LM tiles {BM}x{BN}")
+        _hip.check_tiles(lay, desc, BM, BN)
+
+
 def test_composed_single_terms_match_plain_kinds_bit_exact():
     # {causal, shared_prefix} over the same ids builds the same block mask as
     # the SHARED_PREFIX kind; likewise strip-thinking and causal.
