@@ -73,6 +73,10 @@ def visible_pairs(lay) -> int:
             # history copy: earlier turns, its own user text, itself causally
             tot += a * (hist + u) + a * (a + 1) // 2
         return tot
+    if lay.name == "prefix_lm":
+        # the prefix rows see the whole prefix, every later row keys 0 .. itself
+        return sum(min(P, L) ** 2 + (L * (L + 1) - min(P, L) * (min(P, L) + 1)) // 2
+                   for P, L in zip(lay.notes["prefixes"], lay.seqlens_q))
     if lay.kind == "full":
         return sum(q * k for q, k in zip(lay.seqlens_q, lay.seqlens_k))
     if lay.kind == "causal":

@@ -141,8 +141,51 @@ constexpr int kMaxGroups = 8;
 struct RowGroups {
   int n;                        // number of groups, -1 when over kMaxGroups
   QIds ids[kMaxGroups];
+  int lo[kMaxGroups];           // smallest row (inside the sequence) of each group
   int hi[kMaxGroups];           // largest row (inside the sequence) of each group
 };
+
+// A COMPOSED tile of an OR of several term groups.  The staging pass stores
+// two bytes per key: the query groups that some term group without the
+// causal term lets see the key (okN), and those that some causal term group
+// lets see it (okC).  Pair (i, j), row i in query group g, is then visible
+// iff okN_g(j) or (okC_g(j) and j <= i + off), so for the rows of group g
+// the key is visible to all of them iff okN_g or (okC_g and j <= lo_g + off)
+// and to some of them iff okN_g or (okC_g and j <= hi_g + off): exact, two
+// bytes per key.
+__device__ uint8_t classify_tile_or(const MaskDev& m, const SeqBounds& b, int qlo, int klo, int BM,
+                                    int BN, int n, const int* lo, const int* hi, const uint8_t* okb,
+                                    int k0) {
+  if (qlo >= b.lq || klo >= b.lk) return BMATTN_TILE_EMPTY;
+  const int qhi = min(qlo + BM, b.lq);
+  const int khi = min(klo + BN, b.lk);
+  const bool inside = (qlo + BM <= b.lq) && (klo + BN <= b.lk);
+  const int64_t off = (int64_t)b.lk - b.lq;
+  if (m.causal_all && (int64_t)klo > (int64_t)(qhi - 1) + off) return BMATTN_TILE_EMPTY;
+  const uint32_t every = (1u << n) - 1u;
+  bool all = inside, any = false;
+  for (int j = klo; j < khi; ++j) {
+    // With every term group causal, a key past the last row's position is
+    // hidden from the whole tile (and was not staged).
+    if (m.causal_all && (int64_t)j > (int64_t)(qhi - 1) + off) {
+      all = false;
+      continue;
+    }
+    const uint32_t okn = okb[2 * (j - k0)], okc = okb[2 * (j - k0) + 1];
+    uint32_t to_all = okn, to_some = okn;
+    for (int g = 0; g < n; ++g) {
+      if ((okc >> g) & 1u) {
+        to_all |= (uint32_t)((int64_t)j <= (int64_t)lo[g] + off) << g;
+        to_some |= (uint32_t)((int64_t)j <= (int64_t)hi[g] + off) << g;
+      }
+    }
+    all &= to_all == every;
+    any |= to_some != 0;
+    if (any && !all) return BMATTN_TILE_PARTIAL;
+  }
+  if (!any) return BMATTN_TILE_EMPTY;
+  return all ? BMATTN_TILE_FULL : BMATTN_TILE_PARTIAL;
+}
 
 __device__ uint8_t classify_tile_groups(const MaskDev& m, const SeqBounds& b, int qlo, int klo,
                                         int BM, int BN, int n, const int* hi,
@@ -307,7 +350,8 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev 
         lead[i] = -1 - g;  // a leader holds its group number, encoded below 0
         if (g < kMaxGroups) {
           rg.ids[g] = QIds{qid[i], qturn[i], qdoc[i]};
-          rg.hi[g] = qlo + i;  // rows of the sequence, as the tile bounds
+          rg.lo[g] = qlo + i;  // rows of the sequence, as the tile bounds
+          rg.hi[g] = qlo + i;
         }
       }
       __syncthreads();
@@ -319,8 +363,7 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev 
       const int g = l < 0 ? -1 - l : -1 - lead[l];
       if (g < kMaxGroups) atomicMax(&rg.hi[g], qlo + i);
     }
-    // (an OR of several term groups always enumerates)
-    if (tid == 0) rg.n = (nlead <= kMaxGroups && (m.groups >> 4) == 0) ? nlead : -1;
+    if (tid == 0) rg.n = nlead <= kMaxGroups ? nlead : -1;
     __syncthreads();
   }
 
@@ -333,7 +376,9 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev 
   // for rows with too many groups, four arrays of kw keys.
   const int kw = kKidKeys / 4;
   const bool groups = composed && rg.n >= 0;
-  const int ckeys = !composed ? kKidKeys : (groups ? 4 * kKidKeys : kw);
+  // An OR of several term groups stages two bytes per key (classify_tile_or).
+  const bool multi = composed && (m.groups >> 4) != 0;
+  const int ckeys = !composed ? kKidKeys : (groups ? (multi ? 2 : 4) * kKidKeys : kw);
   const int tpc = std::max(1, std::min(kThreads, ckeys / BN));
   uint8_t* okb = reinterpret_cast<uint8_t*>(kid);
   const int ng = composed ? rg.n : 0;
@@ -342,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev 
   __shared__ uint8_t tand[kThreads], tor[kThreads];
   __shared__ int16_t tcnt[kThreads];
   // (only for 64-key tiles: one wave's lanes then cover one tile)
-  const bool summ = groups && BN == 64;
+  const bool summ = groups && BN == 64 && !multi;
   int hmin = INT32_MAX;
   for (int gi = 0; gi < ng; ++gi) hmin = min(hmin, rg.hi[gi]);
   // With the causal term no key past the row's last query position is
@@ -390,7 +435,20 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev 
         if (j >= kend) continue;
         const KIds k = kb[e];
         const int u = j - kid0;
-        if (groups) {
+        if (groups && multi) {
+          uint32_t okn = 0, okc = 0;
+          for (int32_t gs = m.groups; gs != 0; gs >>= 4) {
+            const int32_t tg = gs & 15;
+            if (tg == 0) continue;
+            uint32_t ok = 0;
+            for (int g = 0; g < ng; ++g)
+              ok |= (uint32_t)composed_ids_ok(tg, m.think_role, rg.ids[g], k.a, k.b, k.c, k.d) << g;
+            if (tg & BMATTN_TERM_CAUSAL) okc |= ok;
+            else okn |= ok;
+          }
+          okb[2 * u] = (uint8_t)okn;
+          okb[2 * u + 1] = (uint8_t)okc;
+        } else if (groups) {
           uint32_t ok = 0;
           for (int g = 0; g < ng; ++g)
             ok |= (uint32_t)composed_ids_ok(m.terms, m.think_role, rg.ids[g], k.a, k.b, k.c, k.d) << g;
@@ -435,6 +493,7 @@ __global__ __launch_bounds__(kThreads) void classify_kernel(MaskDev m, TilesDev 
     if (tid < tpc && bidx < t.n_kt) {
       cls = summ       ? classify_tile_summary(m, b, qlo, bidx * BN, BM, BN, ng, hmin, tand[tid], tor[tid],
                                                tcnt[tid], rg.hi, okb, kid0)
+            : (groups && multi) ? classify_tile_or(m, b, qlo, bidx * BN, BM, BN, ng, rg.lo, rg.hi, okb, kid0)
             : groups   ? classify_tile_groups(m, b, qlo, bidx * BN, BM, BN, ng, rg.hi, okb, kid0)
             : composed ? classify_tile_enum(m, b, qlo, bidx * BN, BM, BN, qid, qturn, qdoc, kid, kw, kid0)
                        : classify_tile(m, b, qlo, bidx * BN, BM, BN, qid, qmin, qmax, kid + tid * (BN + 1));

@@ -231,7 +231,7 @@ def prefix_lm(prefixes=(1024,), lengths=(4096,), H: int = 8, D: int = 128,
     doc = np.concatenate([np.where(np.arange(n) < p, 0, -1) for p, n in zip(prefixes, lens)]
                          ).astype(np.int32) if lens else np.zeros(0, np.int32)
     return Layout("prefix_lm", "composed", dtype, H, D, lens, lens, doc_q=doc, doc_k=doc,
-                  terms=(("causal",), ("document",)))
+                  terms=(("causal",), ("document",)), notes={"prefixes": [int(p) for p in prefixes]})
 
 
 def paged_decode(seed: int = 0, n_seqs: int = 64, lo: int = 512, hi: int = 32768,
@@ -263,6 +263,8 @@ def config(name: str, seed: int = 0) -> Layout:
         return strip_thinking_duplicated()
     if name == "shared_prefix_groups":
         return shared_prefix_groups()
+    if name == "prefix_lm":
+        return prefix_lm((2048,), (8192,), H=16, D=128)
     raise KeyError(name)
 
 

@@ -23,6 +23,7 @@ def _count(lay):
     synth.shared_prefix_groups(n_groups=3, prefix=5, n_suffix=2, suffix=4, pad=3, H=1, D=8),
     synth.paged_decode(seed=1, n_seqs=5, lo=3, hi=50, H=1, D=8),
     synth.Layout("x", "causal", "f32", 1, 8, [3, 5, 1], [7, 5, 2]),
+    synth.prefix_lm(prefixes=(0, 4, 9, 30), lengths=(5, 17, 9, 12), H=1, D=8),
 ])
 def test_closed_forms_match_oracle_small(lay):
     assert bench.visible_pairs(lay) == _count(lay)
@@ -45,4 +46,9 @@ def test_closed_form_duplicated_answers_full_size():
 
 def test_closed_form_shared_prefix_groups_full_size():
     lay = synth.config("shared_prefix_groups")
+    assert bench.visible_pairs(lay) == _count(lay)
+
+
+def test_closed_form_prefix_lm_full_size():
+    lay = synth.config("prefix_lm")
     assert bench.visible_pairs(lay) == _count(lay)

@@ -152,11 +152,11 @@ def test_backward_packed_documents_every_head():
 # Heads checked at full size: eight of the 32 of the shared prefix, four of
 # the others (each head's oracle holds several T x T float64 matrices).
 FULL_SIZE_HEADS = {"shared_prefix": (0, 3, 5, 12, 17, 24, 30, 31), "strip_thinking": (0, 9, 22, 31),
-                   "shared_prefix_groups": (1, 8, 19, 31)}
+                   "shared_prefix_groups": (1, 8, 19, 31), "prefix_lm": (0, 7, 15)}
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["shared_prefix", "strip_thinking", "shared_prefix_groups"])
+@pytest.mark.parametrize("name", ["shared_prefix", "strip_thinking", "shared_prefix_groups", "prefix_lm"])
 def test_backward_single_sequence_workloads(name):
     lay = synth.config(name)
     heads = FULL_SIZE_HEADS[name]

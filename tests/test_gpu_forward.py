@@ -159,7 +159,7 @@ def test_packed_documents_full_size():
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["shared_prefix", "strip_thinking", "strip_thinking_duplicated",
-                                  "shared_prefix_groups"])
+                                  "shared_prefix_groups", "prefix_lm"])
 def test_single_sequence_workloads_every_row_and_head(name):
     # The whole output: every query row of every head against the float64
     # oracle, max-abs and mean-abs over all of O, LSE likewise.

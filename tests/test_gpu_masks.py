@@ -44,7 +44,7 @@ def test_tiles_empty_and_tiny_sequences():
 
 @pytest.mark.parametrize("name", ["causal_f32", "packed_documents", "shared_prefix",
                                   "strip_thinking", "strip_thinking_duplicated",
-                                  "shared_prefix_groups"])
+                                  "shared_prefix_groups", "prefix_lm"])
 def test_tiles_bit_exact_named_workloads(name):
     lay = synth.config(name)
     desc = _hip.desc_for(lay)
