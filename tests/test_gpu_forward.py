@@ -133,6 +133,50 @@ def test_prefix_lm_prefill_decode_and_paged(dtype, D):
     _hip.check_close(od, ld, Od, Ld, dtype, "prefix-LM decode")
 
 
+@pytest.mark.parametrize("paged", [False, True])
+def test_decode_longest_context(paged):
+    # One query over 262 147 keys (4097 kv tiles of 64, 513 splits, a ragged
+    # last page) beside a short sequence, every head.
+    lay = synth.Layout("long_decode", "causal", "bf16", 2, 128, [1, 1], [262147, 5000], paged=paged,
+                       page_size=16)
+    desc = _hip.desc_for(lay)
+    t = bm.build_block_mask(desc, 1, 64)
+    say(f"decode longest context paged={paged}")
+    if paged:
+        q, kp, vp, bt = synth.make_paged_kv(lay, seed=6, device="cpu", extra_pages=1)
+        o, lse = bm.forward(q.to(DEV), kp.to(DEV), vp.to(DEV), desc, t, block_table=bt.to(DEV))
+        O, L = oforward.forward(lay, q, k_pool=kp, v_pool=vp, block_table=bt)
+    else:
+        q, k, v = synth.make_dense_qkv(lay, seed=6, device="cpu")
+        o, lse = bm.forward(q.to(DEV), k.to(DEV), v.to(DEV), desc, t)
+        O, L = oforward.forward(lay, q, k, v)
+    _hip.check_close(o, lse, O, L, "bf16", f"decode 262147 paged={paged}")
+
+
+def test_prefill_longest_causal_row_sampled():
+    # A causal sequence of 65 536 tokens: rows of up to 1024 kv tiles.  The
+    # oracle takes each sampled row as the last query of its own prefix (the
+    # decode form of the causal mask), so no 65 536^2 mask is built.
+    from oracle import attention as oattention
+    from oracle import masks as omasks
+
+    L = 65536
+    lay = synth.causal_single(L=L, H=1, D=128, dtype="bf16")
+    say("prefill 65536-token causal row")
+    o, lse, q, k, v, desc, t = _hip.run_dense(lay, seed=8)
+    rows = sorted({0, 1, 63, 64, 127, 128, 4095, 30000, L - 2, L - 1} |
+                  set(np.random.default_rng(8).integers(0, L, 16).tolist()))
+    qh, kh, vh = (oforward.head_slice(x, 0) for x in (q, k, v))
+    O = np.zeros((len(rows), 1, 128))
+    Lse = np.zeros((1, len(rows)))
+    sc = oattention.default_scale(128)
+    for n, i in enumerate(rows):
+        vis = omasks.visible("causal", 1, i + 1)
+        O[n, 0], Lse[0, n] = (x[0] for x in oattention.three_pass(qh[i:i + 1], kh[:i + 1], vh[:i + 1], vis, sc))
+    idx = torch.tensor(rows)
+    _hip.check_close(o[idx], lse[:, idx], O, Lse, "bf16", "65536 causal rows")
+
+
 def test_empty_sequences_and_rows_without_keys():
     # Sequences of length 0 write nothing; with more queries than keys the
     # first rows see no key: O = 0 and LSE = -inf.
