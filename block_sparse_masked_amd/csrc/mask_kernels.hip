@@ -553,6 +553,75 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(TilesDev t, int rows
   if (r < rows) t.row_order[rank] = r;
 }
 
+// The same ranking from histograms of the counts, when they fit kMaxBins
+// bins: rank of row r with count k = (rows with a count above k) + (rows
+// before r with count k).  Every workgroup counts all rows into `all` and the
+// rows before its own chunk into `before` (LDS atomics on integers, so the
+// counts do not depend on their order), turns `all` into suffix sums, and
+// ranks ties inside its chunk from the chunk's counts in LDS: each thread
+// reads rows / kThreads + kMaxBins / kThreads + kThreads values instead of
+// all rows.
+constexpr int kMaxBins = 4096;
+
+__global__ __launch_bounds__(kThreads) void schedule_hist_kernel(TilesDev t, int rows, int nbins) {
+  __shared__ int32_t all[kMaxBins], before[kMaxBins];
+  __shared__ int32_t key_s[kThreads];
+  __shared__ int32_t wave_sum[kThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c0 = blockIdx.x * kThreads;
+  auto key = [&](int r) { return min(max(t.full_cnt[r] + t.part_cnt[r], 0), nbins - 1); };
+  for (int b = tid; b < nbins; b += kThreads) {
+    all[b] = 0;
+    before[b] = 0;
+  }
+  __syncthreads();
+  for (int r = tid; r < rows; r += kThreads) {
+    const int k = key(r);
+    atomicAdd(&all[k], 1);
+    if (r < c0) atomicAdd(&before[k], 1);
+  }
+  key_s[tid] = c0 + tid < rows ? key(c0 + tid) : -1;
+  __syncthreads();
+  // all[k] <- rows with a count above k: thread tid owns bins
+  // [16 tid, 16 tid + 16); its sum, an inclusive prefix over threads (wave
+  // shuffles, then the wave totals), and a descending pass over its bins.
+  constexpr int kPer = kMaxBins / kThreads;
+  const int b0 = tid * kPer;
+  int own = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) own += (b0 + i < nbins) ? all[b0 + i] : 0;
+  int incl = own;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wave_sum[wave] = incl;
+  __syncthreads();
+  int total = 0, lower = 0;
+  for (int w = 0; w < kThreads / 64; ++w) {
+    total += wave_sum[w];
+    if (w < wave) lower += wave_sum[w];
+  }
+  int above = total - (lower + incl);  // rows in the bins of higher threads
+#pragma unroll
+  for (int i = kPer - 1; i >= 0; --i) {
+    const int b = b0 + i;
+    if (b < nbins) {
+      const int c = all[b];
+      all[b] = above;
+      above += c;
+    }
+  }
+  __syncthreads();
+  const int r = c0 + tid;
+  if (r < rows) {
+    const int k = key_s[tid];
+    int rank = all[k] + before[k];
+    for (int j = 0; j < tid; ++j) rank += key_s[j] == k;
+    t.row_order[rank] = r;
+  }
+}
+
 // Column lists: one workgroup per (sequence s, kv tile b) reads the classes
 // of tiles (a, b) down the column and compacts the FULL and PARTIAL query
 // tiles in ascending a with ballots, as the row lists are compacted.
@@ -818,6 +887,16 @@ __global__ __launch_bounds__(kThreads) void paged_gather_kernel(
 
 }  // namespace
 
+// The row ranking: from count histograms when the counts (0 .. nbins - 1)
+// fit kMaxBins bins, else by comparing every pair of rows.
+hipError_t launch_schedule(const TilesDev& t, int rows, int nbins, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const dim3 grid((rows + kThreads - 1) / kThreads);
+  if (nbins <= kMaxBins) hipLaunchKernelGGL(schedule_hist_kernel, grid, dim3(kThreads), 0, st, t, rows, nbins);
+  else hipLaunchKernelGGL(schedule_kernel, grid, dim3(kThreads), 0, st, t, rows);
+  return hipGetLastError();
+}
+
 hipError_t launch_build_block_mask(const MaskDev& m, const TilesDev& t, hipStream_t st) {
   const int rows = t.n_seqs * t.n_qt;
   const bool small = (m.kind == BMATTN_MASK_FULL || m.kind == BMATTN_MASK_CAUSAL) &&
@@ -829,9 +908,7 @@ hipError_t launch_build_block_mask(const MaskDev& m, const TilesDev& t, hipStrea
   hipLaunchKernelGGL(classify_kernel, dim3(rows), dim3(kThreads), 0, st, m, t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(schedule_kernel, dim3((rows + kThreads - 1) / kThreads), dim3(kThreads), 0,
-                     st, t, rows);
-  return hipGetLastError();
+  return launch_schedule(t, rows, t.n_kt + 1, st);
 }
 
 hipError_t launch_transpose_block_mask(const TilesDev& t, const ColsDev& c, hipStream_t st) {
@@ -845,9 +922,7 @@ hipError_t launch_transpose_block_mask(const TilesDev& t, const ColsDev& c, hipS
   v.full_cnt = c.full_cnt;
   v.part_cnt = c.part_cnt;
   v.row_order = c.col_order;
-  hipLaunchKernelGGL(schedule_kernel, dim3((cols + kThreads - 1) / kThreads), dim3(kThreads), 0, st,
-                     v, cols);
-  return hipGetLastError();
+  return launch_schedule(v, cols, c.n_qt + 1, st);
 }
 
 hipError_t launch_debug_dense_mask(const MaskDev& m, const TilesDev& t, int seq, uint8_t* out,

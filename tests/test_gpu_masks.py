@@ -277,18 +277,23 @@ def test_composed_single_terms_match_plain_kinds_bit_exact():
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("kind", ["causal", "full"])
 @pytest.mark.parametrize("BM,BN", [(128, 64), (1, 64)])
-@pytest.mark.parametrize("layout", ["many_rows", "many_tiles"])
+@pytest.mark.parametrize("layout", ["many_rows", "many_tiles", "many_kv_tiles"])
 def test_tiles_general_classifier_causal_and_full(kind, BM, BN, layout):
     # CAUSAL and FULL masks of more than 1024 tile rows (1100 short
     # sequences) or more than 65 536 tiles (one sequence of 33 000 tokens)
     # take the general classifier, not the one-workgroup path of small masks.
+    # Rows of more than 4095 kv tiles (contexts of 262 144 keys and more) are
+    # ranked by comparing every pair of rows, not from count histograms.
     if layout == "many_rows":
         rng = np.random.default_rng(11 + BM + len(kind))
-        lens = [int(x) for x in rng.integers(1, 300, size=1100)]
+        lens = lens_k = [int(x) for x in rng.integers(1, 300, size=1100)]
+    elif layout == "many_tiles":
+        lens = lens_k = [33000]
     else:
-        lens = [33000]
-    lay = synth.Layout(layout, kind, "bf16", 1, 128, lens, lens)
-    n_qt, n_kt = -(-max(lens) // BM), -(-max(lens) // BN)
+        lens = [5, 1, 130, 3, 64, 200, 7, 2, 33]
+        lens_k = [270000, 262145, 100000, 262143, 262200, 300000, 1000, 270001, 262144]
+    lay = synth.Layout(layout, kind, "bf16", 1, 128, lens, lens_k)
+    n_qt, n_kt = -(-max(lens) // BM), -(-max(lens_k) // BN)
     rows = len(lens) * n_qt
     assert rows > 1024 or rows * n_kt > 65536
     desc = _hip.desc_for(lay)
