@@ -678,7 +678,7 @@ __global__ __launch_bounds__(kThreads) void transpose_kernel(TilesDev t, ColsDev
 // tile classification of classify_tile() restricted to these two kinds.  So
 // the workgroup counts every row, writes the classes and both lists in one
 // flat coalesced pass, and ranks the rows with several threads per row.
-// Same results as classify_kernel followed by schedule_kernel, in one
+// Same results as classify_kernel followed by the row ranking, in one
 // launch.
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallMaxRows = 1024;
