@@ -568,14 +568,14 @@ __global__ __launch_bounds__(kThreads) void schedule_hist_kernel(TilesDev t, int
   __shared__ int32_t key_s[kThreads];
   __shared__ int32_t wave_sum[kThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c0 = blockIdx.x * kThreads;
-  auto key = [&](int r) { return min(max(t.full_cnt[r] + t.part_cnt[r], 0), nbins - 1); };
+  const int64_t c0 = (int64_t)blockIdx.x * kThreads;
+  auto key = [&](int64_t r) { return min(max(t.full_cnt[r] + t.part_cnt[r], 0), nbins - 1); };
   for (int b = tid; b < nbins; b += kThreads) {
     all[b] = 0;
     before[b] = 0;
   }
   __syncthreads();
-  for (int r = tid; r < rows; r += kThreads) {
+  for (int64_t r = tid; r < rows; r += kThreads) {
     const int k = key(r);
     atomicAdd(&all[k], 1);
     if (r < c0) atomicAdd(&before[k], 1);
@@ -613,12 +613,12 @@ __global__ __launch_bounds__(kThreads) void schedule_hist_kernel(TilesDev t, int
     }
   }
   __syncthreads();
-  const int r = c0 + tid;
+  const int64_t r = c0 + tid;
   if (r < rows) {
     const int k = key_s[tid];
     int rank = all[k] + before[k];
     for (int j = 0; j < tid; ++j) rank += key_s[j] == k;
-    t.row_order[rank] = r;
+    t.row_order[rank] = (int32_t)r;
   }
 }
 
@@ -891,7 +891,7 @@ __global__ __launch_bounds__(kThreads) void paged_gather_kernel(
 // fit kMaxBins bins, else by comparing every pair of rows.
 hipError_t launch_schedule(const TilesDev& t, int rows, int nbins, hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  const dim3 grid((rows + kThreads - 1) / kThreads);
+  const dim3 grid((uint32_t)(((int64_t)rows + kThreads - 1) / kThreads));
   if (nbins <= kMaxBins) hipLaunchKernelGGL(schedule_hist_kernel, grid, dim3(kThreads), 0, st, t, rows, nbins);
   else hipLaunchKernelGGL(schedule_kernel, grid, dim3(kThreads), 0, st, t, rows);
   return hipGetLastError();
